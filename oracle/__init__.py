@@ -1,0 +1,288 @@
+"""ctypes wrapper around the C oracle (oracle/ep_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the oracle is the plain CPU statement of what the lattice-rANS codec
+computes.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
+package; the HIP library never links, loads or calls it.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ep_oracle.c")
+LIB = os.path.join(HERE, "_build", "libep_oracle.so")
+
+OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_NONFINITE, ERR_RANGE, ERR_ALPHABET, ERR_CORRUPT, \
+    ERR_VERSION = range(9)
+ERR_CAPACITY = 10
+NTABLES, NBINS = 17, 65536
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no FMA contraction, IEEE semantics)."""
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        L = C.CDLL(LIB)
+        P = C.c_void_p
+        i64, i32, dbl = C.c_int64, C.c_int, C.c_double
+        sig = {
+            "or_widen": (C.c_float, [i32, C.c_uint32]),
+            "or_narrow": (C.c_uint32, [i32, C.c_float]),
+            "or_widen_array": (None, [i32, P, i64, P]),
+            "or_narrow_array": (None, [i32, P, i64, P]),
+            "or_row_sumsq": (None, [i32, P, i64, i64, P]),
+            "or_gain": (C.c_float, [dbl, i64, dbl]),
+            "or_e8_nearest": (i32, [P, P]),
+            "or_e8_brute": (i32, [P, P, P]),
+            "or_e8_certificate": (i64, [P, i64, dbl, P]),
+            "or_e8_vs_brute": (i64, [P, i64, dbl]),
+            "or_e8_mse": (dbl, [P, i64]),
+            "or_fields_from_point": (None, [i32, P, P]),
+            "or_point_from_fields": (None, [P, P]),
+            "or_field_bijection_box": (i64, [i32]),
+            "or_quantize": (i32, [i32, P, i64, i64, P, P, i64, P, P]),
+            "or_histogram": (None, [P, P, i64, P]),
+            "or_normalize": (i32, [P, C.c_int32, i32, P]),
+            "or_build_tables": (i32, [P, i32, P, P, P]),
+            "or_row_lsq": (None, [i32, P, i64, i64, P, P, P, P]),
+            "or_alpha": (C.c_float, [dbl, i64]),
+            "or_encode_tiles": (i32, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, i64]),
+            "or_decode_tiles": (i32, [P, P, P, i64, i32, i32, i32, P, P, P, i64, i64, P, P]),
+            "or_compress": (i32, [i32, P, i64, i64, dbl, i32, dbl, P, i64, P, P]),
+            "or_compress_bound": (i32, [i64, i64, i32, P]),
+            "or_decompress": (i32, [P, i64, i64, i64, P, P, P]),
+            "or_blob_fields": (i32, [P, i64, P, P, P, P, P, P, P, P]),
+            "or_estimate_bpp": (dbl, [i32, P, i64, i64, P, i32, dbl]),
+            "or_search_scale": (dbl, [i32, P, i64, i64, P, i32, dbl]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.c_void_p)
+
+
+# ----------------------------------------------------------------------------------------------
+# numpy-level helpers
+# ----------------------------------------------------------------------------------------------
+def widen(bits: np.ndarray, dtype: int) -> np.ndarray:
+    bits = np.ascontiguousarray(bits)
+    out = np.empty(bits.size, np.float32)
+    lib().or_widen_array(dtype, _p(bits), bits.size, _p(out))
+    return out.reshape(bits.shape)
+
+
+def narrow(values: np.ndarray, dtype: int) -> np.ndarray:
+    v = np.ascontiguousarray(values, np.float32)
+    out = np.empty(v.size, np.uint16 if dtype in (1, 2) else (np.uint8 if dtype == 3 else np.int8))
+    lib().or_narrow_array(dtype, _p(v), v.size, _p(out))
+    return out.reshape(v.shape)
+
+
+def row_sumsq(w: np.ndarray, dtype: int) -> np.ndarray:
+    w = np.ascontiguousarray(w)
+    out = np.empty(w.shape[0], np.float64)
+    lib().or_row_sumsq(dtype, _p(w), w.shape[0], w.shape[1], _p(out))
+    return out
+
+
+def gains(sumsq: np.ndarray, cols: int, s: float) -> np.ndarray:
+    return np.array([lib().or_gain(float(v), cols, s) for v in sumsq], np.float32)
+
+
+def e8_nearest(x: np.ndarray):
+    """x: (..., 8) float32 -> (coset uint8 [...], z int32 [..., 8])."""
+    xs = np.ascontiguousarray(x, np.float32).reshape(-1, 8)
+    cos = np.empty(xs.shape[0], np.uint8)
+    z = np.empty((xs.shape[0], 8), np.int32)
+    L = lib()
+    for i in range(xs.shape[0]):
+        zi = np.empty(8, np.int32)
+        cos[i] = L.or_e8_nearest(_p(xs[i]), _p(zi))
+        z[i] = zi
+    return cos.reshape(x.shape[:-1]), z.reshape(x.shape)
+
+
+def e8_brute(x: np.ndarray):
+    xi = np.ascontiguousarray(x, np.float32).reshape(8)
+    z = np.empty(8, np.int32)
+    d = C.c_longdouble()
+    c = lib().or_e8_brute(_p(xi), _p(z), C.byref(d))
+    return c, z, float(d.value)
+
+
+def fields_from_point(coset: int, z) -> np.ndarray:
+    zi = np.ascontiguousarray(z, np.int32)
+    f = np.empty(8, np.int32)
+    lib().or_fields_from_point(int(coset), _p(zi), _p(f))
+    return f
+
+
+def point_from_fields(f) -> np.ndarray:
+    fi = np.ascontiguousarray(f, np.int32)
+    z = np.empty(8, np.int32)
+    lib().or_point_from_fields(_p(fi), _p(z))
+    return z
+
+
+def quantize(w: np.ndarray, dtype: int, gains_: np.ndarray, row_sel=None):
+    w = np.ascontiguousarray(w)
+    R, Cc = w.shape
+    g = np.ascontiguousarray(gains_, np.float32)
+    if row_sel is not None:
+        sel = np.ascontiguousarray(row_sel, np.int64)
+        nsel = sel.size
+        sel_p = _p(sel)
+    else:
+        nsel, sel_p = R, None
+    nv = nsel * (Cc // 8)
+    cos = np.empty(nv, np.uint8)
+    fld = np.empty(nv * 8, np.int16)
+    st = lib().or_quantize(dtype, _p(w), R, Cc, _p(g), sel_p, nsel, _p(cos), _p(fld))
+    return st, cos, fld
+
+
+def histogram(cos: np.ndarray, fld: np.ndarray) -> np.ndarray:
+    counts = np.empty((NTABLES, NBINS), np.uint64)
+    lib().or_histogram(_p(np.ascontiguousarray(cos)), _p(np.ascontiguousarray(fld)), cos.size,
+                       _p(counts))
+    return counts
+
+
+def normalize(counts, precision: int = 12):
+    c = np.ascontiguousarray(counts, np.uint64)
+    f = np.empty(c.size, np.uint16)
+    st = lib().or_normalize(_p(c), c.size, precision, _p(f))
+    return st, f
+
+
+def build_tables(counts: np.ndarray, precision: int = 12):
+    lo = np.empty(NTABLES, np.int32)
+    n = np.empty(NTABLES, np.uint32)
+    freq = np.zeros((NTABLES, NBINS), np.uint16)
+    st = lib().or_build_tables(_p(np.ascontiguousarray(counts, np.uint64)), precision, _p(lo),
+                               _p(n), _p(freq))
+    return st, lo, n, freq
+
+
+def row_lsq(w: np.ndarray, dtype: int, cos: np.ndarray, fld: np.ndarray):
+    w = np.ascontiguousarray(w)
+    R, Cc = w.shape
+    num = np.empty(R, np.float64)
+    den4 = np.empty(R, np.int64)
+    lib().or_row_lsq(dtype, _p(w), R, Cc, _p(cos), _p(fld), _p(num), _p(den4))
+    return num, den4
+
+
+def alpha(num: float, den4: int) -> float:
+    return lib().or_alpha(float(num), int(den4))
+
+
+def encode_tiles(cos, fld, tile_fields, lanes, precision, lo, n, freq):
+    nv = cos.size
+    V = tile_fields // 8
+    T = (nv + V - 1) // V
+    woff = np.empty(T + 1, np.uint32)
+    states = np.empty(T * lanes, np.uint32)
+    cap = 9 * nv + 1
+    words = np.empty(cap, np.uint16)
+    st = lib().or_encode_tiles(_p(cos), _p(fld), nv, tile_fields, lanes, precision, _p(lo), _p(n),
+                               _p(freq), _p(woff), _p(states), _p(words), cap)
+    return st, woff, states, words[: int(woff[-1])] if st == 0 else words
+
+
+def decode_tiles(woff, states, words, nv, tile_fields, lanes, precision, lo, n, freq, t0=0,
+                 t1=None):
+    V = tile_fields // 8
+    T = (nv + V - 1) // V
+    t1 = T if t1 is None else t1
+    cos = np.zeros(nv, np.uint8)
+    fld = np.zeros(nv * 8, np.int16)
+    words = np.ascontiguousarray(words, np.uint16)
+    if words.size == 0:
+        words = np.zeros(1, np.uint16)
+    st = lib().or_decode_tiles(_p(woff), _p(states), _p(words), nv, tile_fields, lanes, precision,
+                               _p(lo), _p(n), _p(freq), t0, t1, _p(cos), _p(fld))
+    return st, cos, fld
+
+
+def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
+             force_s: float = 0.0):
+    """Returns (status, blob bytes as uint8 array, s)."""
+    w = np.ascontiguousarray(w)
+    R, Cc = w.shape
+    bound = C.c_int64()
+    st = lib().or_compress_bound(R, Cc, tile_fields, C.byref(bound))
+    if st:
+        return st, None, 0.0
+    blob = np.empty(bound.value, np.uint8)
+    nbytes = C.c_int64()
+    s = C.c_double()
+    st = lib().or_compress(dtype, _p(w), R, Cc, float(target_bpp), tile_fields, float(force_s),
+                           _p(blob), blob.size, C.byref(nbytes), C.byref(s))
+    if st:
+        return st, None, s.value
+    return st, blob[: nbytes.value].copy(), s.value
+
+
+def blob_fields(blob: np.ndarray) -> dict:
+    r, c, dt, F, T, s, W, tb = (C.c_int64(), C.c_int64(), C.c_int(), C.c_int(), C.c_int64(),
+                                C.c_double(), C.c_int64(), C.c_int64())
+    st = lib().or_blob_fields(_p(blob), blob.size, C.byref(r), C.byref(c), C.byref(dt),
+                              C.byref(F), C.byref(T), C.byref(s), C.byref(W), C.byref(tb))
+    if st:
+        raise ValueError(f"oracle blob parse failed: {st}")
+    return dict(rows=r.value, cols=c.value, dtype=dt.value, tile_fields=F.value, tiles=T.value,
+                s=s.value, payload_words=W.value, table_bytes=tb.value)
+
+
+def decompress(blob: np.ndarray, t0: int = 0, t1: int = -1, want_fields: bool = False):
+    """Returns (status, out container bits [R, C], coset, fields)."""
+    info = blob_fields(blob)
+    R, Cc, dt = info["rows"], info["cols"], info["dtype"]
+    out = np.zeros((R, Cc), np.uint16 if dt in (1, 2) else (np.uint8 if dt == 3 else np.int8))
+    nv = R * Cc // 8
+    cos = np.zeros(nv, np.uint8) if want_fields else None
+    fld = np.zeros(nv * 8, np.int16) if want_fields else None
+    st = lib().or_decompress(_p(blob), blob.size, t0, t1, _p(out),
+                             _p(cos) if want_fields else None, _p(fld) if want_fields else None)
+    return st, out, cos, fld
+
+
+def estimate_bpp(w, dtype, tile_fields, s, sumsq=None):
+    w = np.ascontiguousarray(w)
+    ss = row_sumsq(w, dtype) if sumsq is None else sumsq
+    return lib().or_estimate_bpp(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields, s)
+
+
+def search_scale(w, dtype, tile_fields, target_bpp, sumsq=None):
+    w = np.ascontiguousarray(w)
+    ss = row_sumsq(w, dtype) if sumsq is None else sumsq
+    return lib().or_search_scale(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
+                                 target_bpp)

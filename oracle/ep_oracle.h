@@ -1,0 +1,94 @@
+/*
+ * CPU ORACLE for the lattice-rANS weight codec -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C implementation of what the EntroPack design page
+ * ("EntroPack lattice compression", sections "Lattice quantization and integer fields",
+ * "Rate selection and refinement", "Encoding and reconstruction") describes, written step by
+ * step in the page's order.  It shares no code with the HIP library and must never be linked
+ * into it: only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load it.
+ *
+ * Every floating-point step runs in a pinned order with no FMA contraction (built with
+ * -ffp-contract=off), so its results are reproducible bit for bit.
+ *
+ * Pins (see tests/test_oracle_*.py): converters vs torch/numpy casts; E8 quantiser vs brute force
+ * and the 240-root certificate and the E8 second moment; field map bijection; table-rule worked
+ * examples; rANS round trip and size bounds; LS scale closed forms; blob size closed form.
+ * The rate search (or_estimate_bpp / or_search_scale) has no pin beyond monotonicity and the
+ * achieved-vs-target report: parity unpinned.
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+enum {
+  OR_OK = 0, OR_ERR_ARG = 1, OR_ERR_SHAPE = 2, OR_ERR_DTYPE = 3, OR_ERR_NONFINITE = 4,
+  OR_ERR_RANGE = 5, OR_ERR_ALPHABET = 6, OR_ERR_CORRUPT = 7, OR_ERR_VERSION = 8,
+  OR_ERR_CAPACITY = 10
+};
+enum { OR_BF16 = 1, OR_FP16 = 2, OR_FP8 = 3, OR_INT8 = 4 };
+
+#define OR_NTABLES 17
+#define OR_NBINS 65536 /* histogram bins per table: value + 32768 */
+
+/* container <-> fp32 */
+float or_widen(int dt, uint32_t bits);
+uint32_t or_narrow(int dt, float y);
+void or_widen_array(int dt, const void* src, int64_t n, float* dst);
+void or_narrow_array(int dt, const float* src, int64_t n, void* dst);
+
+/* row statistics */
+void or_row_sumsq(int dt, const void* w, int64_t rows, int64_t cols, double* out);
+float or_gain(double sumsq, int64_t cols, double s);
+
+/* E8 */
+int or_e8_nearest(const float x[8], int32_t z[8]);
+int or_e8_brute(const float x[8], int32_t z[8], long double* dist);
+long double or_e8_dist_exact(const float x[8], int coset, const int32_t z[8]);
+int64_t or_e8_certificate(const float* x, int64_t nv, double rel_tol, int64_t* n_checked);
+int64_t or_e8_vs_brute(const float* x, int64_t nv, double rel_tol);
+double or_e8_mse(const float* x, int64_t nv);
+void or_fields_from_point(int coset, const int32_t z[8], int32_t f[8]);
+void or_point_from_fields(const int32_t f[8], int32_t z[8]);
+int64_t or_field_bijection_box(int radius);
+
+int or_quantize(int dt, const void* w, int64_t rows, int64_t cols, const float* gains,
+                const int64_t* row_sel, int64_t n_sel, uint8_t* coset, int16_t* fields);
+
+/* model */
+void or_histogram(const uint8_t* coset, const int16_t* fields, int64_t nv, uint64_t* counts);
+int or_normalize(const uint64_t* counts, int32_t n, int precision, uint16_t* freq);
+int or_build_tables(const uint64_t* counts, int precision, int32_t* lo, uint32_t* n,
+                    uint16_t* freq /* [17][65536] */);
+
+/* row least squares */
+void or_row_lsq(int dt, const void* w, int64_t rows, int64_t cols, const uint8_t* coset,
+                const int16_t* fields, double* num, int64_t* den4);
+float or_alpha(double num, int64_t den4);
+
+/* rANS tiles */
+int or_encode_tiles(const uint8_t* coset, const int16_t* fields, int64_t nv, int tile_fields,
+                    int lanes, int precision, const int32_t* lo, const uint32_t* n,
+                    const uint16_t* freq, uint32_t* word_off, uint32_t* states, uint16_t* words,
+                    int64_t words_cap);
+int or_decode_tiles(const uint32_t* word_off, const uint32_t* states, const uint16_t* words,
+                    int64_t nv, int tile_fields, int lanes, int precision, const int32_t* lo,
+                    const uint32_t* n, const uint16_t* freq, int64_t t0, int64_t t1,
+                    uint8_t* coset, int16_t* fields);
+
+/* blob */
+int or_compress(int dt, const void* w, int64_t rows, int64_t cols, double target_bpp,
+                int tile_fields, double force_s, uint8_t* blob, int64_t cap, int64_t* out_bytes,
+                double* s_out);
+int or_compress_bound(int64_t rows, int64_t cols, int tile_fields, int64_t* bytes);
+int or_decompress(const uint8_t* blob, int64_t bytes, int64_t t0, int64_t t1, void* out,
+                  uint8_t* coset_out, int16_t* fields_out);
+int or_blob_fields(const uint8_t* blob, int64_t bytes, int64_t* rows, int64_t* cols, int* dt,
+                   int* tile_fields, int64_t* tiles, double* s, int64_t* payload_words,
+                   int64_t* table_bytes);
+double or_estimate_bpp(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
+                       int tile_fields, double s);
+double or_search_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
+                       int tile_fields, double target_bpp);
+
+#endif

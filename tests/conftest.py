@@ -1,0 +1,30 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test, deselected unless asked for")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
+
+
+def pytest_collection_modifyitems(config, items):
+    if os.environ.get("EP_SLOW"):
+        return
+    skip = pytest.mark.skip(reason="slow test: set EP_SLOW=1 to run")
+    for it in items:
+        if "slow" in it.keywords:
+            it.add_marker(skip)
