@@ -1,0 +1,185 @@
+"""Decode throughput of the lattice-rANS weight codec on one MI355X.
+
+Workload: the 4096 x 4096 bf16 weight with log-normal row scales (sigma_r = exp(N(log 0.02,
+0.5^2))), target 4.0 bits per element, 8192-field tiles -- compressed once by the library, then
+decoded back to bf16 by the fused tile decoder.  One step = one ep_decompress of the whole
+matrix (one kernel launch).  Eight copies of blob + output are rotated so the working set
+(8 x 42 MB) exceeds the 256 MB Infinity Cache and every step reads and writes HBM.
+
+Also timed in the same run: the E8 quantiser + histogram kernel on the same matrix (the
+encoder's GPU hot path), and the CPU oracle's decode (single thread) as a baseline.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE = 8
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decoder shards tiles with no exchange, and no "
+              "multi-GPU run is part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import entropy_coded_weight_ep_amd as ep
+    import ep_synth as S
+
+    wl = S.WORKLOADS[2]
+    R, C, F, target = wl["rows"], wl["cols"], wl["tile_fields"], wl["target_bpp"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w_bits = S.workload_weights(2)
+    t = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # compress once (library: GPU rate search, quantiser, histogram, LS scales; host encoder)
+    t0 = time.time()
+    comp = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F))
+    compress_s = time.time() - t0
+    info = comp.info
+    blob_bytes = int(comp.blob.size)
+    out_bytes = R * C * 2
+
+    # rotated copies of blob, decode tables and outputs
+    blobs, tabs, outs = [], [], []
+    for i in range(ROTATE):
+        d = torch.from_numpy(comp.blob).to(dev)
+        tb = torch.empty(ep.EP_DEC_TABLE_BYTES, dtype=torch.uint8, device=dev)
+        assert ep.ep_prepare_decode(d, info, tb) == 0
+        blobs.append(d)
+        tabs.append(tb)
+        outs.append(torch.empty((R, C), dtype=torch.bfloat16, device=dev))
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k = i % ROTATE
+        st = ep.ep_decompress(blobs[k], info, tabs[k], outs[k], err)
+        if st:
+            raise ep.EPError(st, "ep_decompress")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert int(err.item()) == 0, "decode reported a corrupt tile"
+
+    # quality of the decoded tensor (relative L2 against the input, as in the design page usage)
+    ref = t.float()
+    rel_l2 = ((outs[(args.steps - 1) % ROTATE].float() - ref).norm() / ref.norm()).item()
+
+    # E8 quantiser + histogram on the same matrix at the selected scale (gains from the blob's s)
+    sumsq = torch.empty(R, dtype=torch.float64, device=dev)
+    assert ep.ep_row_sumsq(t, ep.EP_BF16, R, C, sumsq) == 0
+    rms = torch.sqrt(sumsq / C)
+    gains = torch.where(rms > 0, 1.0 / (rms * comp.scale), torch.zeros_like(rms)).float()
+    cos = torch.empty(R * C // 8, dtype=torch.uint8, device=dev)
+    fld = torch.empty(R * C, dtype=torch.int16, device=dev)
+    hist = torch.empty(ep.HIST_BYTES // 4, dtype=torch.int32, device=dev)
+    qerr = torch.zeros(1, dtype=torch.int32, device=dev)
+    qsteps = max(10, args.steps // 4)
+    for _ in range(3):
+        ep.ep_quantize_e8(t, ep.EP_BF16, R, C, gains, None, R, cos, fld, hist, qerr)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(qsteps):
+        ep.ep_quantize_e8(t, ep.EP_BF16, R, C, gains, None, R, cos, fld, hist, qerr)
+    ev1.record()
+    torch.cuda.synchronize()
+    q_ms = ev0.elapsed_time(ev1) / qsteps
+    q_bytes = R * C * 2 + R * C // 8 + R * C * 2        # read weights, write cosets + fields
+
+    value = out_bytes / (ms * 1e-3) / 1e9
+    algo_bytes = blob_bytes + out_bytes
+    achieved = algo_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "decoded weight GB/s/GPU (output bytes) + % of HBM roofline; actual_bpp",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "4096x4096 bf16, log-normal row scales (mu=log 0.02, sigma=0.5), "
+                        "target 4.0 bpp, 8192-field tiles, one fused decode per step",
+            "rows": R, "cols": C, "container": "bf16", "tile_fields": F,
+            "target_bpp": target, "actual_bpp": round(info.actual_bpp, 5),
+            "scale": comp.scale, "rel_l2": round(rel_l2, 6),
+            "blob_bytes": blob_bytes, "output_bytes": out_bytes,
+            "rotated_copies": ROTATE, "compress_seconds": round(compress_s, 3),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_decode<16, bf16>",
+            "bytes_per_launch": algo_bytes,
+        },
+        "quantize": {
+            "kernel": "k_quantize_e8<bf16> + histogram",
+            "ms": round(q_ms, 6), "bytes_per_launch": q_bytes,
+            "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
+            "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(comp.blob, out_bytes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(blob, out_bytes, min_seconds):
+    """The CPU oracle's decode of the same blob (single thread), repeated for >= min_seconds."""
+    import oracle
+
+    oracle.build(force=False)
+    reps, t0 = 0, time.time()
+    while True:
+        st, _, _, _ = oracle.decompress(blob)
+        assert st == 0
+        reps += 1
+        if time.time() - t0 >= min_seconds:
+            break
+    el = time.time() - t0
+    return {
+        "value": round(out_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole 4096x4096 blob decoded {reps} times in {el:.1f} s (single thread)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,6 @@
+// Fused tile decoder instantiated for the fp16 container (kernels in ep_decode.h).
+#include "ep_decode.h"
+
+namespace ep {
+template hipError_t launch_decode<EP_FP16>(const DecodeArgs&, int, bool, bool, size_t, hipStream_t);
+}  // namespace ep

@@ -1,0 +1,6 @@
+// Fused tile decoder instantiated for the int8 container (kernels in ep_decode.h).
+#include "ep_decode.h"
+
+namespace ep {
+template hipError_t launch_decode<EP_INT8>(const DecodeArgs&, int, bool, bool, size_t, hipStream_t);
+}  // namespace ep

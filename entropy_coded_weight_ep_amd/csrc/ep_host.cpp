@@ -1,0 +1,598 @@
+// Host side of libep.so: table normalisation, the interleaved rANS tile encoder, the blob
+// format, the sampled-row rate search and the compress driver.
+//
+// Sources: EntroPack design page "EntroPack lattice compression" -- "Lattice quantization and
+// integer fields" (coset-conditioned model), "Rate selection and refinement" (sampled-row size
+// estimate incl. metadata, per-row least squares), "Encoding and reconstruction" (rANS in
+// independently decodable tiles; stored tables, row scales, tile metadata; actual_bpp).
+// rANS: Duda, "Asymmetric numeral systems" (arXiv 0902.0271); several states sharing one word
+// stream: Giesen, "Interleaved entropy coders" (arXiv 1402.3392).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace {
+
+constexpr uint32_t kM = 1u << EP_PRECISION;
+constexpr uint32_t kL = 1u << 16;
+constexpr int kK = EP_LANES;
+constexpr int kHeaderBytes = 64;
+
+inline int64_t round16(int64_t b) { return (b + 15) / 16 * 16; }
+inline int64_t record_bytes(uint32_t n) { return (8 + 2 * (int64_t)n + 3) / 4 * 4; }
+
+int64_t tables_bytes(const uint32_t* n) {
+  int64_t b = 0;
+  for (int t = 0; t < EP_NTABLES; t++) b += record_bytes(n[t]);
+  return round16(b);
+}
+
+struct Layout {
+  int64_t tables, alpha, word_off, states, words, total;
+};
+
+Layout layout(int64_t rows, int64_t tiles, int64_t table_bytes, int64_t words) {
+  Layout L;
+  L.tables = kHeaderBytes;
+  L.alpha = L.tables + table_bytes;
+  L.word_off = L.alpha + round16(4 * rows);
+  L.states = L.word_off + round16(4 * (tiles + 1));
+  L.words = L.states + round16(4 * (int64_t)kK * tiles);
+  L.total = L.words + round16(2 * words);
+  return L;
+}
+
+// Frequencies summing to M for one table's counts (rule documented in ep.h, ep_build_tables).
+ep_status normalise(const uint32_t* cnt, uint32_t n, uint16_t* out) {
+  uint64_t total = 0;
+  uint32_t distinct = 0;
+  for (uint32_t i = 0; i < n; i++) {
+    total += cnt[i];
+    distinct += cnt[i] != 0;
+  }
+  if (distinct > kM) return EP_ERR_ALPHABET;
+  std::vector<int64_t> f(n, 0);
+  int64_t assigned = 0;
+  for (uint32_t i = 0; i < n; i++) {
+    if (!cnt[i]) continue;
+    f[i] = std::max<int64_t>(1, (int64_t)(((uint64_t)cnt[i] * kM) / total));
+    assigned += f[i];
+  }
+  int64_t gap = (int64_t)kM - assigned;
+  if (gap > 0) {
+    uint32_t top = 0;
+    for (uint32_t i = 1; i < n; i++)
+      if (cnt[i] > cnt[top]) top = i;
+    f[top] += gap;
+  }
+  while (gap < 0) {
+    int64_t top = -1;
+    for (uint32_t i = 0; i < n; i++)
+      if (f[i] > 1 && (top < 0 || f[i] > f[top])) top = i;
+    const int64_t take = std::min(-gap, f[top] - 1);
+    f[top] -= take;
+    gap += take;
+  }
+  for (uint32_t i = 0; i < n; i++) out[i] = (uint16_t)f[i];
+  return EP_OK;
+}
+
+// Per-table symbol lookups for the encoder.
+struct EncTable {
+  int32_t lo = 0;
+  uint32_t n = 0;
+  std::vector<uint32_t> freq, cum;
+};
+
+std::vector<EncTable> enc_tables(const ep_tables* T) {
+  std::vector<EncTable> out(EP_NTABLES);
+  for (int t = 0; t < EP_NTABLES; t++) {
+    EncTable& e = out[t];
+    e.lo = T->lo[t];
+    e.n = T->n[t];
+    e.freq.resize(e.n);
+    e.cum.resize(e.n);
+    uint32_t c = 0;
+    for (uint32_t i = 0; i < e.n; i++) {
+      e.freq[i] = T->freq[(size_t)t * EP_HIST_BINS + i];
+      e.cum[i] = c;
+      c += e.freq[i];
+    }
+  }
+  return out;
+}
+
+// Encode one tile into `stream` (forward word order) and its 64 final states.
+bool encode_tile(const uint8_t* cs, const int16_t* fs, int64_t v0, int64_t nvt, int J,
+                 const std::vector<EncTable>& tabs, uint32_t* states,
+                 std::vector<uint16_t>& scratch, std::vector<uint16_t>& stream) {
+  uint32_t x[kK];
+  std::fill(x, x + kK, kL);
+  scratch.clear();
+  for (int phase = 8; phase >= 0; --phase) {
+    for (int j = J - 1; j >= 0; --j) {
+      for (int l = kK - 1; l >= 0; --l) {
+        const int64_t u = l + (int64_t)kK * j;
+        if (u >= nvt) continue;
+        const int64_t v = v0 + u;
+        const int c = cs[v];
+        const EncTable& tb = (phase == 0) ? tabs[0] : tabs[1 + 8 * c + (phase - 1)];
+        const int32_t value = (phase == 0) ? c : fs[8 * v + (phase - 1)];
+        const int64_t s = (int64_t)value - tb.lo;
+        if (s < 0 || s >= (int64_t)tb.n || tb.freq[s] == 0) return false;
+        const uint32_t f = tb.freq[s];
+        uint32_t xs = x[l];
+        if ((uint64_t)xs >= ((uint64_t)f << (32 - EP_PRECISION))) {
+          scratch.push_back((uint16_t)xs);
+          xs >>= 16;
+        }
+        x[l] = (xs / f) * kM + (xs % f) + tb.cum[s];
+      }
+    }
+  }
+  stream.insert(stream.end(), scratch.rbegin(), scratch.rend());
+  std::copy(x, x + kK, states);
+  return true;
+}
+
+struct Hip {
+  hipError_t e = hipSuccess;
+  bool ok() const { return e == hipSuccess; }
+  void operator()(hipError_t r) {
+    if (e == hipSuccess) e = r;
+  }
+};
+
+}  // namespace
+
+// ==========================================================================================
+extern "C" const char* ep_status_string(ep_status st) {
+  switch (st) {
+    case EP_OK: return "ok";
+    case EP_ERR_ARG: return "invalid argument";
+    case EP_ERR_SHAPE: return "unsupported shape (cols must be a multiple of 8)";
+    case EP_ERR_DTYPE: return "unsupported container dtype";
+    case EP_ERR_NONFINITE: return "input holds NaN or infinity";
+    case EP_ERR_RANGE: return "lattice coordinate outside the int16 field range";
+    case EP_ERR_ALPHABET: return "more than 2^P distinct symbols in one table";
+    case EP_ERR_CORRUPT: return "corrupt blob or tile";
+    case EP_ERR_VERSION: return "unsupported blob version or parameters";
+    case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_CAPACITY: return "buffer too small";
+  }
+  return "unknown status";
+}
+
+extern "C" void ep_config_default(ep_config* cfg) {
+  if (!cfg) return;
+  cfg->target_bpp = 4.0;
+  cfg->tile_fields = 8192;
+  cfg->sample_rows = 256;
+  cfg->search_iters = 40;
+  cfg->refine = 0;
+  cfg->force_scale = 0.0;
+}
+
+extern "C" ep_status ep_build_tables(const ep_hist* h_hist, uint32_t precision_bits,
+                                     ep_tables* h_out) {
+  if (!h_hist || !h_out) return EP_ERR_ARG;
+  if (precision_bits != EP_PRECISION) return EP_ERR_ARG;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    const uint32_t* c = h_hist->counts + (size_t)t * EP_HIST_BINS;
+    int first = -1, last = -1;
+    for (int b = 0; b < EP_HIST_BINS; b++) {
+      if (c[b]) {
+        if (first < 0) first = b;
+        last = b;
+      }
+    }
+    uint16_t* f = h_out->freq + (size_t)t * EP_HIST_BINS;
+    if (first < 0) {
+      h_out->lo[t] = 0;
+      h_out->n[t] = 0;
+      continue;
+    }
+    h_out->lo[t] = first - 32768;
+    h_out->n[t] = (uint32_t)(last - first + 1);
+    const ep_status st = normalise(c + first, h_out->n[t], f);
+    if (st != EP_OK) return st;
+  }
+  return EP_OK;
+}
+
+extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t cols,
+                                  int64_t n_sample_rows, uint32_t tile_fields) {
+  if (!h_hist || rows < 1 || cols < 8 || n_sample_rows < 1) return INFINITY;
+  std::vector<ep_tables> tv(1);
+  ep_tables& T = tv[0];
+  if (ep_build_tables(h_hist, EP_PRECISION, &T) != EP_OK) return INFINITY;
+  double acc = 0.0;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    const uint32_t* c = h_hist->counts + (size_t)t * EP_HIST_BINS + (T.lo[t] + 32768);
+    for (uint32_t i = 0; i < T.n[t]; i++) {
+      if (!c[i]) continue;
+      const double f = (double)T.freq[(size_t)t * EP_HIST_BINS + i];
+      acc = acc + (double)c[i] * ((double)EP_PRECISION - std::log2(f));
+    }
+  }
+  const double bits = acc * ((double)rows / (double)n_sample_rows);
+  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
+  const Layout L = layout(rows, tiles, tables_bytes(T.n), 0);
+  const double meta = (double)L.words;      // everything before the payload words
+  return (bits + 8.0 * meta) / ((double)rows * (double)cols);
+}
+
+extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fields,
+                                     int64_t n_vectors, uint32_t tile_fields,
+                                     const ep_tables* tables, uint32_t* h_word_off,
+                                     uint32_t* h_states, uint16_t* h_words, int64_t words_cap) {
+  if (!h_coset || !h_fields || !tables || !h_word_off || !h_states || !h_words) return EP_ERR_ARG;
+  if (tile_fields < 512 || tile_fields % 512 || n_vectors < 1) return EP_ERR_ARG;
+  const int64_t V = tile_fields / 8, tiles = (n_vectors + V - 1) / V;
+  const int J = (int)(V / kK);
+  const std::vector<EncTable> tabs = enc_tables(tables);
+  unsigned nth = std::max(1u, std::thread::hardware_concurrency());
+  nth = (unsigned)std::min<int64_t>(nth, tiles);
+  // each worker encodes a contiguous tile range into its own stream
+  std::vector<std::vector<uint16_t>> streams(nth);
+  std::vector<std::vector<uint32_t>> counts(nth);
+  std::vector<int> ok(nth, 1);
+  auto work = [&](unsigned w) {
+    const int64_t t0 = tiles * w / nth, t1 = tiles * (w + 1) / nth;
+    std::vector<uint16_t> scratch;
+    scratch.reserve(9 * V);
+    for (int64_t t = t0; t < t1; t++) {
+      const size_t before = streams[w].size();
+      const int64_t v0 = t * V, nvt = std::min<int64_t>(V, n_vectors - v0);
+      if (!encode_tile(h_coset, h_fields, v0, nvt, J, tabs, h_states + t * kK, scratch,
+                       streams[w])) {
+        ok[w] = 0;
+        return;
+      }
+      counts[w].push_back((uint32_t)(streams[w].size() - before));
+    }
+  };
+  std::vector<std::thread> pool;
+  for (unsigned w = 1; w < nth; w++) pool.emplace_back(work, w);
+  work(0);
+  for (auto& th : pool) th.join();
+  for (unsigned w = 0; w < nth; w++)
+    if (!ok[w]) return EP_ERR_ARG;
+  int64_t pos = 0, t = 0;
+  for (unsigned w = 0; w < nth; w++) {
+    if (pos + (int64_t)streams[w].size() > words_cap) return EP_ERR_CAPACITY;
+    std::memcpy(h_words + pos, streams[w].data(), streams[w].size() * 2);
+    for (uint32_t c : counts[w]) {
+      h_word_off[t++] = (uint32_t)pos;
+      pos += c;
+    }
+  }
+  h_word_off[tiles] = (uint32_t)pos;
+  return EP_OK;
+}
+
+extern "C" ep_status ep_compress_bound(int64_t rows, int64_t cols, uint32_t tile_fields,
+                                       size_t* bytes) {
+  if (!bytes) return EP_ERR_ARG;
+  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (tile_fields < 512 || tile_fields % 512) return EP_ERR_ARG;
+  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
+  uint32_t nmax[EP_NTABLES];
+  for (int t = 0; t < EP_NTABLES; t++) nmax[t] = 65535;
+  *bytes = (size_t)layout(rows, tiles, tables_bytes(nmax), 9 * nv).total;
+  return EP_OK;
+}
+
+namespace {
+struct Workspace {
+  ep_hist* hist;
+  double* sumsq;
+  float* gains;
+  int64_t* rows_sel;
+  double* num;
+  int64_t* den4;
+  uint32_t* err;
+  uint8_t* coset;
+  int16_t* fields;
+  size_t total;
+};
+
+Workspace carve(void* base, int64_t rows, int64_t cols) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t o = 0;
+  Workspace w;
+  const int64_t nv = rows * (cols / 8);
+  w.hist = reinterpret_cast<ep_hist*>(p + o); o += up(sizeof(ep_hist));
+  w.sumsq = reinterpret_cast<double*>(p + o); o += up(8 * rows);
+  w.gains = reinterpret_cast<float*>(p + o); o += up(4 * rows);
+  w.rows_sel = reinterpret_cast<int64_t*>(p + o); o += up(8 * (size_t)std::min<int64_t>(rows, 1 << 20));
+  w.num = reinterpret_cast<double*>(p + o); o += up(8 * rows);
+  w.den4 = reinterpret_cast<int64_t*>(p + o); o += up(8 * rows);
+  w.err = reinterpret_cast<uint32_t*>(p + o); o += up(4);
+  w.coset = p + o; o += up(nv);
+  w.fields = reinterpret_cast<int16_t*>(p + o); o += up(2 * 8 * nv);
+  w.total = o;
+  return w;
+}
+
+inline float row_gain(double sumsq, int64_t cols, double s) {
+  const double rms = std::sqrt(sumsq / (double)cols);
+  if (rms == 0.0) return 0.0f;
+  return (float)(1.0 / (rms * s));
+}
+}  // namespace
+
+extern "C" size_t ep_compress_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 8) return 0;
+  return carve(nullptr, rows, cols).total;
+}
+
+extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_info* out) {
+  if (!h_blob || !out) return EP_ERR_ARG;
+  const uint8_t* b = static_cast<const uint8_t*>(h_blob);
+  if (bytes < (size_t)kHeaderBytes || std::memcmp(b, "EPK1", 4) != 0) return EP_ERR_CORRUPT;
+  uint16_t version;
+  std::memcpy(&version, b + 4, 2);
+  if (version != 1) return EP_ERR_VERSION;
+  ep_blob_info I;
+  std::memset(&I, 0, sizeof I);
+  I.dtype = b[6];
+  I.precision = b[7];
+  uint64_t u64;
+  uint32_t u32;
+  std::memcpy(&u64, b + 8, 8); I.rows = (int64_t)u64;
+  std::memcpy(&u64, b + 16, 8); I.cols = (int64_t)u64;
+  std::memcpy(&u32, b + 24, 4); I.tile_fields = (int32_t)u32;
+  std::memcpy(&u32, b + 28, 4); I.lanes = (int32_t)u32;
+  std::memcpy(&u32, b + 32, 4); I.tiles = u32;
+  uint32_t tb;
+  std::memcpy(&tb, b + 36, 4);
+  std::memcpy(&I.scale, b + 40, 8);
+  std::memcpy(&u64, b + 48, 8); I.payload_words = (int64_t)u64;
+  std::memcpy(&I.max_tile_words, b + 56, 4);
+  if (I.dtype < EP_BF16 || I.dtype > EP_INT8) return EP_ERR_DTYPE;
+  if (I.precision != EP_PRECISION || I.lanes != EP_LANES) return EP_ERR_VERSION;
+  if (I.rows < 1 || I.cols < 8 || I.cols % 8 || I.tile_fields < 512 || I.tile_fields % 512)
+    return EP_ERR_CORRUPT;
+  if (I.rows > ((int64_t)1 << 40) || I.cols > ((int64_t)1 << 40)) return EP_ERR_CORRUPT;
+  const int64_t nv = I.rows * (I.cols / 8), V = I.tile_fields / 8;
+  if (I.tiles != (nv + V - 1) / V) return EP_ERR_CORRUPT;
+  if (I.payload_words < 0 || I.payload_words > ((int64_t)1 << 32)) return EP_ERR_CORRUPT;
+  const Layout L = layout(I.rows, I.tiles, tb, I.payload_words);
+  if ((int64_t)bytes != L.total) return EP_ERR_CORRUPT;
+  int64_t p = L.tables;
+  bool big = false;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    if (p + 8 > L.alpha) return EP_ERR_CORRUPT;
+    int32_t lo;
+    uint32_t n;
+    std::memcpy(&lo, b + p, 4);
+    std::memcpy(&n, b + p + 4, 4);
+    if (n > 65535 || p + record_bytes(n) > L.alpha) return EP_ERR_CORRUPT;
+    uint32_t sum = 0;
+    for (uint32_t i = 0; i < n; i++) {
+      uint16_t f;
+      std::memcpy(&f, b + p + 8 + 2 * i, 2);
+      sum += f;
+    }
+    if (n && sum != kM) return EP_ERR_CORRUPT;
+    if (t == 0) {
+      // coset table: one or two symbols inside {0, 1}
+      if (n < 1 || n > 2 || lo < 0 || lo + (int64_t)n > 2) return EP_ERR_CORRUPT;
+      uint16_t f0;
+      std::memcpy(&f0, b + p + 8, 2);
+      if (f0 == 0) return EP_ERR_CORRUPT;
+      I.coset_freq0 = f0;
+    } else if (n > 0 && (lo < -64 || lo + (int64_t)n - 1 > 63)) {
+      big = true;                 // field values do not all fit the 7-bit slot-entry value
+    }
+    I.table_off[t] = p;
+    I.lo[t] = lo;
+    I.n[t] = n;
+    p += record_bytes(n);
+  }
+  if (round16(p - L.tables) != (int64_t)tb) return EP_ERR_CORRUPT;
+  const uint32_t* off = reinterpret_cast<const uint32_t*>(b + L.word_off);
+  if (off[0] != 0 || (int64_t)off[I.tiles] != I.payload_words) return EP_ERR_CORRUPT;
+  uint32_t maxw = 0;
+  for (int64_t t = 0; t < I.tiles; t++) {
+    if (off[t + 1] < off[t]) return EP_ERR_CORRUPT;
+    maxw = std::max(maxw, off[t + 1] - off[t]);
+  }
+  if (maxw != I.max_tile_words) return EP_ERR_CORRUPT;
+  I.big_alphabet = big ? 1u : 0u;
+  I.bytes = (int64_t)bytes;
+  I.actual_bpp = 8.0 * (double)bytes / ((double)I.rows * (double)I.cols);
+  I.off_tables = L.tables;
+  I.off_alpha = L.alpha;
+  I.off_word_off = L.word_off;
+  I.off_states = L.states;
+  I.off_words = L.words;
+  *out = I;
+  return EP_OK;
+}
+
+extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
+                                 const ep_config* cfg, void* d_workspace, size_t workspace_bytes,
+                                 void* h_blob, size_t cap, size_t* out_bytes, double* scale_out,
+                                 void* stream) {
+  if (!d_w || !cfg || !d_workspace || !h_blob || !out_bytes) return EP_ERR_ARG;
+  if (dtype < EP_BF16 || dtype > EP_INT8) return EP_ERR_DTYPE;
+  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  const uint32_t F = cfg->tile_fields;
+  if (F < 512 || F % 512) return EP_ERR_ARG;
+  if (cfg->refine) return EP_ERR_ARG;
+  const bool forced = cfg->force_scale > 0.0;
+  if (!forced && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
+                   cfg->target_bpp <= 11.0))
+    return EP_ERR_ARG;
+  const int64_t nv = rows * (cols / 8);
+  if (nv >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
+  if (workspace_bytes < ep_compress_workspace_bytes(rows, cols)) return EP_ERR_CAPACITY;
+  const Workspace ws = carve(d_workspace, rows, cols);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Hip hip;
+  ep_status st;
+
+  // 1. row RMS
+  std::vector<double> sumsq(rows);
+  if ((st = ep_row_sumsq(d_w, dtype, rows, cols, ws.sumsq, stream)) != EP_OK) return st;
+  hip(hipMemcpyAsync(sumsq.data(), ws.sumsq, 8 * rows, hipMemcpyDeviceToHost, s));
+  hip(hipStreamSynchronize(s));
+  if (!hip.ok()) return EP_ERR_HIP;
+  for (double v : sumsq)
+    if (!std::isfinite(v)) return EP_ERR_NONFINITE;
+
+  std::vector<ep_hist> hist_host(1);
+  std::vector<float> gains(rows, 0.0f);
+  uint32_t err_host = 0;
+
+  // quantise (a subset of) rows at scale sc and fetch the histogram; returns the error bits
+  auto quantise = [&](double sc, const int64_t* d_sel, int64_t nsel, const std::vector<int64_t>& sel)
+      -> uint32_t {
+    if (d_sel) {
+      for (int64_t r : sel) gains[r] = row_gain(sumsq[r], cols, sc);
+    } else {
+      for (int64_t r = 0; r < rows; r++) gains[r] = row_gain(sumsq[r], cols, sc);
+    }
+    uint32_t zero = 0;
+    hip(hipMemcpyAsync(ws.gains, gains.data(), 4 * rows, hipMemcpyHostToDevice, s));
+    hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
+    const ep_status q = ep_quantize_e8(d_w, dtype, rows, cols, ws.gains, d_sel, nsel, ws.coset,
+                                       ws.fields, ws.hist, ws.err, stream);
+    if (q != EP_OK) return 1u << q;
+    hip(hipMemcpyAsync(hist_host[0].counts, ws.hist->counts, sizeof(ep_hist),
+                       hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+    hip(hipStreamSynchronize(s));
+    if (!hip.ok()) return 1u << EP_ERR_HIP;
+    return err_host;
+  };
+
+  // 2. rate search on sampled rows
+  double sc;
+  if (forced) {
+    sc = cfg->force_scale;
+  } else {
+    const int64_t ns = std::min<int64_t>(std::min<int64_t>(rows, std::max<uint32_t>(1, cfg->sample_rows)),
+                                         (int64_t)1 << 20);
+    std::vector<int64_t> sel(ns);
+    for (int64_t i = 0; i < ns; i++) sel[i] = (i * rows) / ns;
+    hip(hipMemcpyAsync(ws.rows_sel, sel.data(), 8 * ns, hipMemcpyHostToDevice, s));
+    auto est = [&](double scale) -> double {
+      const uint32_t e = quantise(scale, ws.rows_sel, ns, sel);
+      if (e & (1u << EP_ERR_HIP)) return NAN;
+      if (e) return INFINITY;
+      return ep_estimate_bpp(hist_host.data(), rows, cols, ns, F);
+    };
+    double lo = -20.0, hi = 12.0;
+    const double target = cfg->target_bpp;
+    double e_hi = est(std::exp2(hi));
+    if (std::isnan(e_hi)) return EP_ERR_HIP;
+    if (e_hi > target) {
+      sc = std::exp2(hi);
+    } else {
+      const double e_lo = est(std::exp2(lo));
+      if (std::isnan(e_lo)) return EP_ERR_HIP;
+      if (e_lo <= target) {
+        sc = std::exp2(lo);
+      } else {
+        for (uint32_t it = 0; it < cfg->search_iters; it++) {
+          const double mid = 0.5 * (lo + hi);
+          const double e = est(std::exp2(mid));
+          if (std::isnan(e)) return EP_ERR_HIP;
+          if (e <= target) hi = mid;
+          else lo = mid;
+        }
+        sc = std::exp2(hi);
+      }
+    }
+  }
+  if (scale_out) *scale_out = sc;
+
+  // 3. full quantisation + histogram
+  {
+    const std::vector<int64_t> none;
+    const uint32_t e = quantise(sc, nullptr, rows, none);
+    if (e & (1u << EP_ERR_HIP)) return EP_ERR_HIP;
+    if (e & (1u << EP_ERR_RANGE)) return EP_ERR_RANGE;
+    if (e) return EP_ERR_ARG;
+  }
+  // 4. row least-squares scales
+  std::vector<double> num(rows);
+  std::vector<int64_t> den4(rows);
+  if ((st = ep_row_lsq(d_w, dtype, rows, cols, ws.coset, ws.fields, ws.num, ws.den4, stream)) != EP_OK)
+    return st;
+  std::vector<uint8_t> coset(nv);
+  std::vector<int16_t> fields(8 * nv);
+  hip(hipMemcpyAsync(num.data(), ws.num, 8 * rows, hipMemcpyDeviceToHost, s));
+  hip(hipMemcpyAsync(den4.data(), ws.den4, 8 * rows, hipMemcpyDeviceToHost, s));
+  hip(hipMemcpyAsync(coset.data(), ws.coset, nv, hipMemcpyDeviceToHost, s));
+  hip(hipMemcpyAsync(fields.data(), ws.fields, 16 * nv, hipMemcpyDeviceToHost, s));
+  hip(hipStreamSynchronize(s));
+  if (!hip.ok()) return EP_ERR_HIP;
+  std::vector<float> alpha(rows);
+  for (int64_t r = 0; r < rows; r++)
+    alpha[r] = den4[r] == 0 ? 0.0f : (float)(num[r] / ((double)den4[r] / 4.0));
+
+  // 5. tables
+  std::vector<ep_tables> tabv(1);
+  ep_tables& T = tabv[0];
+  if ((st = ep_build_tables(hist_host.data(), EP_PRECISION, &T)) != EP_OK) return st;
+
+  // 6. tiles
+  const int64_t V = F / 8, tiles = (nv + V - 1) / V;
+  std::vector<uint32_t> word_off(tiles + 1), states(tiles * kK);
+  std::vector<uint16_t> words(9 * nv + 1);
+  if ((st = ep_encode_tiles(coset.data(), fields.data(), nv, F, &T, word_off.data(),
+                            states.data(), words.data(), (int64_t)words.size())) != EP_OK)
+    return st;
+  const int64_t W = word_off[tiles];
+
+  // 7. blob
+  const int64_t tb = tables_bytes(T.n);
+  const Layout L = layout(rows, tiles, tb, W);
+  *out_bytes = (size_t)L.total;
+  if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
+  uint8_t* b = static_cast<uint8_t*>(h_blob);
+  std::memset(b, 0, (size_t)L.total);
+  std::memcpy(b, "EPK1", 4);
+  const uint16_t version = 1;
+  std::memcpy(b + 4, &version, 2);
+  b[6] = (uint8_t)dtype;
+  b[7] = EP_PRECISION;
+  const uint64_t r64 = (uint64_t)rows, c64 = (uint64_t)cols, w64 = (uint64_t)W;
+  const uint32_t f32 = F, k32 = kK, t32 = (uint32_t)tiles, tb32 = (uint32_t)tb;
+  uint32_t maxw = 0;
+  for (int64_t t = 0; t < tiles; t++) maxw = std::max(maxw, word_off[t + 1] - word_off[t]);
+  std::memcpy(b + 8, &r64, 8);
+  std::memcpy(b + 16, &c64, 8);
+  std::memcpy(b + 24, &f32, 4);
+  std::memcpy(b + 28, &k32, 4);
+  std::memcpy(b + 32, &t32, 4);
+  std::memcpy(b + 36, &tb32, 4);
+  std::memcpy(b + 40, &sc, 8);
+  std::memcpy(b + 48, &w64, 8);
+  std::memcpy(b + 56, &maxw, 4);
+  int64_t p = L.tables;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    std::memcpy(b + p, &T.lo[t], 4);
+    std::memcpy(b + p + 4, &T.n[t], 4);
+    std::memcpy(b + p + 8, T.freq + (size_t)t * EP_HIST_BINS, 2 * (size_t)T.n[t]);
+    p += record_bytes(T.n[t]);
+  }
+  std::memcpy(b + L.alpha, alpha.data(), 4 * rows);
+  std::memcpy(b + L.word_off, word_off.data(), 4 * (tiles + 1));
+  std::memcpy(b + L.states, states.data(), 4 * kK * tiles);
+  std::memcpy(b + L.words, words.data(), 2 * W);
+  return EP_OK;
+}

@@ -1,0 +1,463 @@
+// HIP kernels (gfx950) of the lattice-rANS weight codec and their C-ABI entry points.
+//
+// What is computed follows the EntroPack design page "EntroPack lattice compression"
+// (sections "Lattice quantization and integer fields" and "Encoding and reconstruction") and the
+// EntroPack abstract (fused GPU symbol decoding and weight reconstruction; BF16/FP16/FP8/INT8
+// containers).  The kernels are written for CDNA4: wave64, LDS-staged tables and words,
+// wavefront ballot/prefix renormalisation, 16-byte stores.
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -ffp-contract=off (the E8 quantiser and the row sums
+// must round every product and sum separately so that their results are reproducible).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+// ------------------------------------------------------------------------------------------
+// Row sums of squares: one lane per row, left-to-right fp64 accumulation (each square is exact
+// in fp64 for every container, so the sum is reproducible).  A 64-row x 64-column tile is
+// staged through LDS so the global reads are row-contiguous.
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, int64_t rows,
+                                                  int64_t cols, double* __restrict__ out) {
+  __shared__ float tile[64][65];
+  const int lane = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  double acc = 0.0;
+  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
+    const int64_t nc = (cols - c0 < 64) ? cols - c0 : 64;
+    for (int rr = 0; rr < 64; rr++) {
+      const int64_t r = r0 + rr;
+      float v = 0.0f;
+      if (r < rows && lane < nc) {
+        const int64_t i = r * cols + c0 + lane;
+        uint32_t bits = (DT == EP_BF16 || DT == EP_FP16)
+                            ? (uint32_t)static_cast<const uint16_t*>(w)[i]
+                            : (uint32_t)static_cast<const uint8_t*>(w)[i];
+        v = widen<DT>(bits);
+      }
+      tile[rr][lane] = v;
+    }
+    __syncthreads();
+    if (r0 + lane < rows) {
+      for (int cc = 0; cc < nc; cc++) {
+        double v = (double)tile[lane][cc];
+        acc = __dadd_rn(acc, __dmul_rn(v, v));
+      }
+    }
+    __syncthreads();
+  }
+  if (r0 + lane < rows) out[r0 + lane] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// E8 nearest point (Conway & Sloane 1982 fast quantiser for D8 u (D8 + 1/2)): round each
+// coordinate half-to-even; if the coordinate sum is odd, move the worst-rounded coordinate
+// (lowest index among equals) one step towards x (upwards for a zero residual).  Candidates
+// for x and for x - 1/2; the closer one wins, coset 0 on ties.  Every operation is a single
+// IEEE fp32 op (no contraction), distances summed e0^2 + e1^2 + ... in index order.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void d8_round(const float u[8], float a[8]) {
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a[i] = __builtin_rintf(u[i]);
+    sum += (int32_t)a[i];
+  }
+  if (sum & 1) {
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) r[i] = __fsub_rn(u[i], a[i]);
+    int k = 0;
+    float best = __builtin_fabsf(r[0]);
+#pragma unroll
+    for (int i = 1; i < 8; i++) {
+      float d = __builtin_fabsf(r[i]);
+      if (d > best) { best = d; k = i; }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (i == k) a[i] = (r[i] >= 0.0f) ? a[i] + 1.0f : a[i] - 1.0f;
+  }
+}
+
+__device__ __forceinline__ float sqdist8(const float x[8], const float p[8]) {
+  float e = __fsub_rn(x[0], p[0]);
+  float d = __fmul_rn(e, e);
+#pragma unroll
+  for (int i = 1; i < 8; i++) {
+    e = __fsub_rn(x[i], p[i]);
+    d = __fadd_rn(d, __fmul_rn(e, e));
+  }
+  return d;
+}
+
+// Returns the coset; z receives the D8 part (p - coset/2).
+__device__ __forceinline__ int e8_nearest(const float x[8], int32_t z[8]) {
+  float A[8], u[8], Bz[8], B[8];
+  d8_round(x, A);
+#pragma unroll
+  for (int i = 0; i < 8; i++) u[i] = __fsub_rn(x[i], 0.5f);
+  d8_round(u, Bz);
+#pragma unroll
+  for (int i = 0; i < 8; i++) B[i] = __fadd_rn(Bz[i], 0.5f);
+  const float dA = sqdist8(x, A);
+  const float dB = sqdist8(x, B);
+  const int c = (dA <= dB) ? 0 : 1;
+#pragma unroll
+  for (int i = 0; i < 8; i++) z[i] = (int32_t)(c ? Bz[i] : A[i]);
+  return c;
+}
+
+// Histogram privatisation window in LDS: values [-128, 127] of every table.
+constexpr int kHistWin = 256;
+constexpr int kHistOff = 128;
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = v;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_quantize_e8(
+    const void* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ gain,
+    const int64_t* __restrict__ row_index, uint32_t n_vec, uint32_t vpr,
+    uint8_t* __restrict__ coset, int16_t* __restrict__ fields, uint32_t* __restrict__ hist,
+    uint32_t* __restrict__ err) {
+  __shared__ uint32_t sh[EP_NTABLES * kHistWin];
+  const bool do_hist = hist != nullptr;
+  if (do_hist) {
+    for (int i = threadIdx.x; i < EP_NTABLES * kHistWin; i += 256) sh[i] = 0;
+    __syncthreads();
+  }
+  bool bad = false, bad_row = false;
+  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < n_vec; v += gridDim.x * 256u) {
+    const uint32_t i = v / vpr;
+    const uint32_t m = v - i * vpr;
+    const int64_t r = row_index ? row_index[i] : (int64_t)i;
+    if (r < 0 || r >= rows) {                // a row index outside the tensor: skip, report
+      bad_row = true;
+      continue;
+    }
+    float x[8];
+    load8<DT>(w, r * cols + 8 * (int64_t)m, x);
+    const float g = gain[r];
+    bool out_of_range = false;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      x[k] = __fmul_rn(x[k], g);
+      out_of_range |= !(__builtin_fabsf(x[k]) <= 65536.0f);
+    }
+    if (out_of_range) {
+#pragma unroll
+      for (int k = 0; k < 8; k++) x[k] = 0.0f;
+    }
+    int32_t z[8];
+    int c = e8_nearest(x, z);
+#pragma unroll
+    for (int k = 0; k < 8; k++) out_of_range |= (z[k] > 32767) | (z[k] < -32767);
+    if (out_of_range) {                      // flagged; keep every field (and bin) in range
+      c = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) z[k] = 0;
+    }
+    bad |= out_of_range;
+    int32_t f[8];
+#pragma unroll
+    for (int k = 0; k < 7; k++) f[k] = z[k];
+    f[7] = z[7] >> 1;                                   // arithmetic shift = floor(z7 / 2)
+    coset[v] = (uint8_t)c;
+    uint4 pk;
+    pk.x = (uint32_t)(f[0] & 0xFFFF) | ((uint32_t)f[1] << 16);
+    pk.y = (uint32_t)(f[2] & 0xFFFF) | ((uint32_t)f[3] << 16);
+    pk.z = (uint32_t)(f[4] & 0xFFFF) | ((uint32_t)f[5] << 16);
+    pk.w = (uint32_t)(f[6] & 0xFFFF) | ((uint32_t)f[7] << 16);
+    reinterpret_cast<uint4*>(fields)[v] = pk;
+    if (do_hist) {
+      atomicAdd(&sh[kHistOff + c], 1u);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int t = 1 + 8 * c + k;
+        const int32_t val = f[k];
+        if (val >= -kHistOff && val < kHistWin - kHistOff)
+          atomicAdd(&sh[t * kHistWin + val + kHistOff], 1u);
+        else
+          atomicAdd(&hist[(int64_t)t * EP_HIST_BINS + (val + 32768)], 1u);
+      }
+    }
+  }
+  if (bad) atomicOr(err, 1u << EP_ERR_RANGE);
+  if (bad_row) atomicOr(err, 1u << EP_ERR_ARG);
+  if (do_hist) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < EP_NTABLES * kHistWin; i += 256) {
+      const uint32_t cnt = sh[i];
+      if (cnt) {
+        const int t = i / kHistWin;
+        const int val = i % kHistWin - kHistOff;
+        atomicAdd(&hist[(int64_t)t * EP_HIST_BINS + (val + 32768)], cnt);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Row least-squares terms: one lane per row; 64 rows x 64 columns (8 vectors) per LDS stage.
+// num = sum w * p (fp64, left to right; each product exact), den4 = sum (2p)^2 (int64).
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int64_t rows,
+                                                int64_t cols, const uint8_t* __restrict__ coset,
+                                                const int16_t* __restrict__ fields,
+                                                double* __restrict__ num,
+                                                int64_t* __restrict__ den4) {
+  __shared__ float sw[64][65];
+  __shared__ int16_t sf[64][66];
+  __shared__ uint8_t sc[64][9];
+  const int lane = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t vpr = cols / 8;
+  double acc = 0.0;
+  int64_t d4 = 0;
+  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
+    const int64_t nc = (cols - c0 < 64) ? cols - c0 : 64;
+    for (int rr = 0; rr < 64; rr++) {
+      const int64_t r = r0 + rr;
+      float v = 0.0f;
+      int16_t f = 0;
+      if (r < rows && lane < nc) {
+        const int64_t i = r * cols + c0 + lane;
+        uint32_t bits = (DT == EP_BF16 || DT == EP_FP16)
+                            ? (uint32_t)static_cast<const uint16_t*>(w)[i]
+                            : (uint32_t)static_cast<const uint8_t*>(w)[i];
+        v = widen<DT>(bits);
+        f = fields[i];
+      }
+      sw[rr][lane] = v;
+      sf[rr][lane] = f;
+      if (lane < 8) sc[rr][lane] = (r < rows && lane < nc / 8) ? coset[r * vpr + c0 / 8 + lane] : 0;
+    }
+    __syncthreads();
+    if (r0 + lane < rows) {
+      for (int m = 0; m < nc / 8; m++) {
+        const int32_t c = sc[lane][m];
+        int32_t par = 0;
+        for (int k = 0; k < 7; k++) par ^= sf[lane][8 * m + k];
+        for (int k = 0; k < 8; k++) {
+          int32_t z = sf[lane][8 * m + k];
+          if (k == 7) z = 2 * z + (par & 1);
+          const int64_t h = 2 * (int64_t)z + c;
+          const double p = (double)h * 0.5;
+          acc = __dadd_rn(acc, __dmul_rn((double)sw[lane][8 * m + k], p));
+          d4 += h * h;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (r0 + lane < rows) {
+    num[r0 + lane] = acc;
+    den4[r0 + lane] = d4;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-table expansion (once per blob).  For each of the 16 field tables, slot s of [0, 2^P)
+// belongs to the value v with cum(v) <= s < cum(v) + f(v) and gets
+//   entry = f | (s - cum) << 13 | (v & 127) << 25        (32 bits)
+//   value = v                                             (int16, used for wide alphabets)
+// The 7-bit value in the entry is exact whenever every field value lies in [-64, 63].
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict__ blob,
+                                                       TableArgs ta, uint32_t* __restrict__ ent,
+                                                       int16_t* __restrict__ val) {
+  __shared__ uint32_t scan[256];
+  const int t = blockIdx.x;                    // field table 0..15 = blob table 1 + t
+  const uint32_t n = ta.n[1 + t];
+  const int32_t lo = ta.lo[1 + t];
+  const uint16_t* freq = reinterpret_cast<const uint16_t*>(blob + ta.off[1 + t] + 8);
+  uint32_t* E = ent + (size_t)t * kM;
+  int16_t* S = val + (size_t)t * kM;
+  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; }
+  __syncthreads();
+  uint32_t base = 0;
+  for (uint32_t c0 = 0; c0 < n; c0 += 256) {
+    const uint32_t s = c0 + threadIdx.x;
+    const uint32_t f = (s < n) ? freq[s] : 0u;
+    scan[threadIdx.x] = f;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      uint32_t add = (threadIdx.x >= (unsigned)d) ? scan[threadIdx.x - d] : 0u;
+      __syncthreads();
+      scan[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const uint32_t cum = base + scan[threadIdx.x] - f;
+    const int32_t v = lo + (int32_t)s;
+    for (uint32_t q = 0; q < f; q++) {
+      const uint32_t slot = cum + q;
+      if (slot < kM) {
+        E[slot] = f | (q << 13) | (((uint32_t)v & 127u) << 25);
+        S[slot] = (int16_t)v;
+      }
+    }
+    base += scan[255];
+    __syncthreads();
+  }
+}
+
+}  // namespace ep
+
+// ==========================================================================================
+// C-ABI entry points that launch kernels
+// ==========================================================================================
+using namespace ep;
+
+static bool valid_dtype(int32_t dt) { return dt >= EP_BF16 && dt <= EP_INT8; }
+
+extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
+                                  double* d_out, void* stream) {
+  if (!d_w || !d_out) return EP_ERR_ARG;
+  if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
+  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + 63) / 64));
+  switch (dtype) {
+    case EP_BF16: k_row_sumsq<EP_BF16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+    case EP_FP16: k_row_sumsq<EP_FP16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+    case EP_FP8_E4M3FN: k_row_sumsq<EP_FP8_E4M3FN><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+    default: k_row_sumsq<EP_INT8><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+  }
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
+                                    const float* d_row_gain, const int64_t* d_row_index,
+                                    int64_t n_rows_sel, uint8_t* d_coset, int16_t* d_fields,
+                                    ep_hist* d_hist, uint32_t* d_err, void* stream) {
+  if (!d_w || !d_row_gain || !d_coset || !d_fields || !d_err) return EP_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
+    return EP_ERR_ARG;
+  if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
+  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  const int64_t nsel = d_row_index ? n_rows_sel : rows;
+  if (nsel < 0 || (d_row_index && nsel > (int64_t)1 << 31)) return EP_ERR_ARG;
+  const int64_t nvec = nsel * (cols / 8);
+  if (nvec >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hist = d_hist ? d_hist->counts : nullptr;
+  if (hist) {
+    k_fill_u32<<<1024, 256, 0, s>>>(hist, (int64_t)EP_NTABLES * EP_HIST_BINS, 0u);
+  }
+  if (nvec == 0) return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid((unsigned)blocks);
+  const uint32_t nv = (uint32_t)nvec, vpr = (uint32_t)(cols / 8);
+#define EP_Q(DT) k_quantize_e8<DT><<<grid, 256, 0, s>>>(d_w, rows, cols, d_row_gain, d_row_index, nv, \
+                                                        vpr, d_coset, d_fields, hist, d_err)
+  switch (dtype) {
+    case EP_BF16: EP_Q(EP_BF16); break;
+    case EP_FP16: EP_Q(EP_FP16); break;
+    case EP_FP8_E4M3FN: EP_Q(EP_FP8_E4M3FN); break;
+    default: EP_Q(EP_INT8); break;
+  }
+#undef EP_Q
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
+                                const uint8_t* d_coset, const int16_t* d_fields, double* d_num,
+                                int64_t* d_den4, void* stream) {
+  if (!d_w || !d_coset || !d_fields || !d_num || !d_den4) return EP_ERR_ARG;
+  if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
+  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + 63) / 64));
+#define EP_L(DT) k_row_lsq<DT><<<grid, 64, 0, s>>>(d_w, rows, cols, d_coset, d_fields, d_num, d_den4)
+  switch (dtype) {
+    case EP_BF16: EP_L(EP_BF16); break;
+    case EP_FP16: EP_L(EP_FP16); break;
+    case EP_FP8_E4M3FN: EP_L(EP_FP8_E4M3FN); break;
+    default: EP_L(EP_INT8); break;
+  }
+#undef EP_L
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* info,
+                                       void* d_dec_tables, void* stream) {
+  if (!d_blob || !info || !d_dec_tables) return EP_ERR_ARG;
+  TableArgs ta;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    ta.off[t] = info->table_off[t];
+    ta.n[t] = info->n[t];
+    ta.lo[t] = info->lo[t];
+  }
+  uint32_t* ent = static_cast<uint32_t*>(d_dec_tables);
+  int16_t* sym = reinterpret_cast<int16_t*>(ent + 16 * kM);
+  k_expand_tables<<<16, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(d_blob), ta, ent, sym);
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+
+extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
+                                   const void* d_dec_tables, void* d_out, uint32_t* d_err,
+                                   void* stream) {
+  if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_blob) & 15u) || (reinterpret_cast<uintptr_t>(d_out) & 15u))
+    return EP_ERR_ARG;
+  if (info->precision != EP_PRECISION || info->lanes != EP_LANES) return EP_ERR_VERSION;
+  if (info->dtype < EP_BF16 || info->dtype > EP_INT8) return EP_ERR_DTYPE;
+  const int J = info->tile_fields / (8 * EP_LANES);
+  if (info->tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
+  const int64_t nv = info->rows * info->cols / 8;
+  if (nv >= ((int64_t)1 << 31) || info->tiles < 1) return EP_ERR_SHAPE;
+  DecodeArgs a;
+  const uint8_t* b = static_cast<const uint8_t*>(d_blob);
+  a.alpha = reinterpret_cast<const float*>(b + info->off_alpha);
+  a.word_off = reinterpret_cast<const uint32_t*>(b + info->off_word_off);
+  a.states = reinterpret_cast<const uint32_t*>(b + info->off_states);
+  a.words = reinterpret_cast<const uint16_t*>(b + info->off_words);
+  a.ent = static_cast<const uint32_t*>(d_dec_tables);
+  a.val = reinterpret_cast<const int16_t*>(a.ent + 16 * kM);
+  a.out = d_out;
+  a.err = d_err;
+  a.n_vec = (uint32_t)nv;
+  a.vpr = (uint32_t)(info->cols / 8);
+  a.inv_vpr = 1.0 / (double)a.vpr;
+  a.max_tile_words = info->max_tile_words;
+  // words region per wave: the aligned chunks of the largest tile plus one wave of slack
+  a.words_stride = ((info->max_tile_words + 7u + 7u) & ~7u) + 64u;
+  for (int t = 0; t < EP_NTABLES; t++) a.lo[t] = info->lo[t];
+  a.coset_f0 = info->coset_freq0;
+  const bool big = info->big_alphabet != 0;
+  const size_t lds = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0) +
+                     (size_t)kDecWaves * a.words_stride * 2;
+  if (lds > 160 * 1024) return EP_ERR_VERSION;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t tiles = (uint32_t)info->tiles;
+  const uint32_t V = (uint32_t)info->tile_fields / 8;
+  const bool last_ragged = (uint64_t)tiles * V != (uint64_t)nv;
+  const uint32_t full_tiles = last_ragged ? tiles - 1 : tiles;
+  auto launch = [&](uint32_t t0, uint32_t t1, bool ragged) -> hipError_t {
+    a.tile_begin = t0;
+    a.tile_end = t1;
+    switch (info->dtype) {
+      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, lds, s);
+      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, lds, s);
+      case EP_FP8_E4M3FN: return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, lds, s);
+      default: return launch_decode<EP_INT8>(a, J, big, ragged, lds, s);
+    }
+  };
+  if (full_tiles > 0 && launch(0, full_tiles, false) != hipSuccess) return EP_ERR_HIP;
+  if (last_ragged && launch(tiles - 1, tiles, true) != hipSuccess) return EP_ERR_HIP;
+  return EP_OK;
+}

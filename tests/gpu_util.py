@@ -1,0 +1,132 @@
+"""Helpers for the GPU tests: move numpy buffers to the device and call the C ABI of libep.so.
+Nothing here computes any part of the codec."""
+
+import sys
+
+import numpy as np
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ep_mod():
+    import entropy_coded_weight_ep_amd as ep
+
+    ep.lib()
+    return ep
+
+
+def dev(a: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def zeros_u8(n):
+    import torch
+
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device="cuda")
+
+
+def gpu_row_sumsq(w: np.ndarray, dtype: int) -> np.ndarray:
+    import torch
+
+    ep = ep_mod()
+    R, C = w.shape
+    d_w = dev(w.view(np.uint8))
+    out = torch.zeros(R, dtype=torch.float64, device="cuda")
+    st = ep.ep_row_sumsq(d_w, dtype, R, C, out)
+    assert st == 0, st
+    return host(out)
+
+
+def gpu_quantize(w: np.ndarray, dtype: int, gains: np.ndarray, row_sel=None, with_hist=True):
+    """Returns (err word, coset, fields, hist) from ep_quantize_e8."""
+    import torch
+
+    ep = ep_mod()
+    R, C = w.shape
+    d_w = dev(w.view(np.uint8))
+    d_g = dev(np.ascontiguousarray(gains, np.float32))
+    if row_sel is not None:
+        d_sel = dev(np.ascontiguousarray(row_sel, np.int64))
+        nsel = len(row_sel)
+    else:
+        d_sel, nsel = None, R
+    nv = nsel * (C // 8)
+    d_cos = torch.zeros(max(nv, 1), dtype=torch.uint8, device="cuda")
+    d_fld = torch.zeros(max(nv * 8, 8), dtype=torch.int16, device="cuda")
+    d_hist = torch.zeros(ep.HIST_BYTES // 4, dtype=torch.int32, device="cuda") if with_hist else None
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = ep.ep_quantize_e8(d_w, dtype, R, C, d_g, d_sel, nsel, d_cos, d_fld, d_hist, d_err)
+    assert st == 0, st
+    torch.cuda.synchronize()
+    hist = host(d_hist).view(np.uint32).reshape(17, 65536) if with_hist else None
+    return int(host(d_err)[0]), host(d_cos)[:nv], host(d_fld)[:nv * 8], hist
+
+
+def gpu_row_lsq(w: np.ndarray, dtype: int, cos: np.ndarray, fld: np.ndarray):
+    import torch
+
+    ep = ep_mod()
+    R, C = w.shape
+    num = torch.zeros(R, dtype=torch.float64, device="cuda")
+    den4 = torch.zeros(R, dtype=torch.int64, device="cuda")
+    st = ep.ep_row_lsq(dev(w.view(np.uint8)), dtype, R, C, dev(cos), dev(fld), num, den4)
+    assert st == 0, st
+    return host(num), host(den4)
+
+
+class GpuBlob:
+    """A blob on the device with its decode tables prepared."""
+
+    def __init__(self, blob: np.ndarray):
+        import torch
+
+        ep = ep_mod()
+        self.blob = blob
+        st, self.info = ep.ep_blob_parse(blob)
+        assert st == 0, st
+        self.d_blob = dev(blob)
+        self.d_tab = torch.zeros(ep.EP_DEC_TABLE_BYTES, dtype=torch.uint8, device="cuda")
+        assert ep.ep_prepare_decode(self.d_blob, self.info, self.d_tab) == 0
+
+    def out_bytes(self):
+        esize = 2 if self.info.dtype in (1, 2) else 1
+        return self.info.rows * self.info.cols * esize
+
+    def decode(self, d_out=None):
+        """Returns (err word, output container bits as numpy [rows, cols])."""
+        import torch
+
+        ep = ep_mod()
+        if d_out is None:
+            d_out = torch.zeros(self.out_bytes(), dtype=torch.uint8, device="cuda")
+        d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        st = ep.ep_decompress(self.d_blob, self.info, self.d_tab, d_out, d_err)
+        assert st == 0, st
+        torch.cuda.synchronize()
+        out = host(d_out)
+        dt = self.info.dtype
+        npdt = np.uint16 if dt in (1, 2) else (np.uint8 if dt == 3 else np.int8)
+        return int(host(d_err)[0]), out.view(npdt).reshape(self.info.rows, self.info.cols)
+
+
+def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
+                 force_scale: float = 0.0):
+    """Library compress of a device copy of w -> (blob bytes, s)."""
+    import torch
+
+    ep = ep_mod()
+    tmap = {1: torch.bfloat16, 2: torch.float16, 3: torch.float8_e4m3fn, 4: torch.int8}
+    t = dev(w.view(np.uint8)).view(tmap[dtype]).view(w.shape)
+    cfg = ep.LatticeRANSConfig(target_bpp=target_bpp, tile_fields=tile_fields,
+                               force_scale=force_scale)
+    c = ep.compress(t, cfg)
+    return c.blob, c.scale

@@ -1,0 +1,158 @@
+"""CPU tests of libep.so: the library loads, exports every call declared in include/ep.h, and its
+host-side logic (table normalisation, tile encoder, blob parser, rate estimate) matches the oracle
+bit for bit.  No kernel is launched here."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ep_synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ep():
+    import entropy_coded_weight_ep_amd as ep
+
+    if not os.path.exists(ep.lib_path()):
+        pytest.skip("libep.so not built (run __graft_entry__.build())")
+    ep.lib()
+    return ep
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "ep.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(ep_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(ep):
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = ep.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ep.ABI), "binding and header disagree"
+
+
+def test_status_strings_and_defaults(ep):
+    for st in range(11):
+        assert ep.ep_status_string(st)
+    cfg = ep.ep_config_default()
+    assert cfg.tile_fields == 8192 and cfg.sample_rows == 256 and cfg.search_iters == 40
+    assert cfg.refine == 0
+
+
+def _hist_uint32(counts):
+    return np.ascontiguousarray(counts.astype(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_build_tables_matches_oracle(ep, orc, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    nv = int(g.integers(100, 5000))
+    cos = (g.random(nv) < 0.3).astype(np.uint8)
+    spread = [0.5, 2.0, 10.0, 60.0, 300.0, 1500.0][seed]
+    fld = np.clip(np.rint(g.standard_t(3, nv * 8) * spread), -32767, 32767).astype(np.int16)
+    counts = orc.histogram(cos, fld)
+    st_o, lo_o, n_o, freq_o = orc.build_tables(counts)
+    st, lo, n, freq = ep.ep_build_tables(_hist_uint32(counts))
+    assert st == st_o
+    if st == 0:
+        assert np.array_equal(lo, lo_o) and np.array_equal(n, n_o)
+        assert np.array_equal(freq, freq_o)
+
+
+def test_build_tables_alphabet_error(ep, orc):
+    counts = np.zeros((17, 65536), np.uint64)
+    counts[0, 32768] = 10
+    counts[1, 32768 - 3000:32768 + 1097] = 1          # 4097 distinct values
+    st, *_ = ep.ep_build_tables(_hist_uint32(counts))
+    assert st == ep.EP_ERR_ALPHABET
+    assert orc.build_tables(counts)[0] == orc.ERR_ALPHABET
+
+
+@pytest.mark.parametrize("nv,F", [(512, 4096), (5000, 4096), (40, 8192), (3000, 16384),
+                                  (2048, 8192)])
+def test_encode_tiles_matches_oracle(ep, orc, nv, F):
+    g = np.random.Generator(np.random.PCG64(nv))
+    cos = (g.random(nv) < 0.45).astype(np.uint8)
+    fld = np.rint(g.standard_normal(nv * 8) * 3).astype(np.int16)
+    counts = orc.histogram(cos, fld)
+    st, lo, n, freq = orc.build_tables(counts)
+    st_o, woff_o, states_o, words_o = orc.encode_tiles(cos, fld, F, 64, 12, lo, n, freq)
+    st, woff, states, words = ep.ep_encode_tiles(cos, fld, F, ep.tables_struct(lo, n, freq))
+    assert st == 0 and st_o == 0
+    assert np.array_equal(woff, woff_o)
+    assert np.array_equal(states, states_o)
+    assert np.array_equal(words, words_o)
+
+
+@pytest.mark.parametrize("key,shape", [(1, None), (2, (64, 1024)), (3, (64, 512)),
+                                       ("5a", (16, 2048)), ("5b", (16, 2048))])
+def test_blob_parse_on_oracle_blobs(ep, orc, key, shape):
+    wl = S.WORKLOADS[key]
+    R, Cc = shape or (wl["rows"], wl["cols"])
+    w = S.workload_weights(key, R, Cc)
+    st, blob, s = orc.compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"])
+    assert st == 0
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0
+    ref = orc.blob_fields(blob)
+    assert (info.rows, info.cols, info.dtype, info.tile_fields, info.tiles) == \
+        (ref["rows"], ref["cols"], ref["dtype"], ref["tile_fields"], ref["tiles"])
+    assert info.scale == ref["s"] and info.payload_words == ref["payload_words"]
+    assert info.actual_bpp == 8.0 * blob.size / (R * Cc)
+    # the table records as written by the oracle
+    p = 64
+    for t in range(17):
+        lo = int(blob[p:p + 4].view(np.int32)[0])
+        n = int(blob[p + 4:p + 8].view(np.uint32)[0])
+        assert info.lo[t] == lo and info.n[t] == n and info.table_off[t] == p
+        if t == 0:
+            assert info.coset_freq0 == int(blob[p + 8:p + 10].view(np.uint16)[0])
+        p += (8 + 2 * n + 3) // 4 * 4
+
+
+def test_blob_parse_rejects_corruption(ep, orc):
+    w = S.workload_weights(1)
+    st, blob, s = orc.compress(w, S.BF16, 3.5, 4096)
+    assert ep.ep_blob_parse(blob)[0] == 0
+    b = blob.copy(); b[0] = 0
+    assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_CORRUPT
+    b = blob.copy(); b[4] = 7
+    assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_VERSION
+    assert ep.ep_blob_parse(blob[:-16].copy())[0] == ep.EP_ERR_CORRUPT
+    b = blob.copy(); b[64 + 8] ^= 1                       # coset frequencies no longer sum to M
+    assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_CORRUPT
+    b = blob.copy(); b[6] = 9
+    assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_DTYPE
+
+
+@pytest.mark.parametrize("s", [0.05, 0.3, 1.0, 4.0])
+def test_estimate_matches_oracle(ep, orc, s):
+    w = S.lognormal_rows(600, 512, seed=4)
+    R, Cc = w.shape
+    ns = 256
+    sel = (np.arange(ns) * R) // ns
+    ss = orc.row_sumsq(w, S.BF16)
+    g = orc.gains(ss, Cc, s)
+    st, cos, fld = orc.quantize(w, S.BF16, g, row_sel=sel)
+    assert st == 0
+    counts = orc.histogram(cos, fld)
+    est = ep.ep_estimate_bpp(_hist_uint32(counts), R, Cc, ns, 4096)
+    assert est == orc.estimate_bpp(w, S.BF16, 4096, s)
+
+
+def test_compress_bound_covers_blobs(ep, orc):
+    for key, shape in [(1, None), (3, (64, 512))]:
+        wl = S.WORKLOADS[key]
+        R, Cc = shape or (wl["rows"], wl["cols"])
+        w = S.workload_weights(key, R, Cc)
+        st, blob, s = orc.compress(w, wl["dtype"], 11.0, wl["tile_fields"])
+        assert blob.size <= ep.ep_compress_bound(R, Cc, wl["tile_fields"])
+    with pytest.raises(ep.EPError):
+        ep.ep_compress_bound(4, 12, 4096)

@@ -1,0 +1,223 @@
+"""GPU parity: every HIP kernel of libep.so against the CPU oracle, element by element, on seeded
+synthetic inputs (integer and byte results bit-exact; the fp64 row sums and the decoded
+containers are bit-exact as well, since both sides use the same rounded operations in the same
+order).
+
+Sizes span several tiles and ragged tails; the full-size workloads are in
+test_gpu_fullsize.py.  Inputs come from ep_synth; expected values only from the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import ep_synth as S
+from gpu_util import GpuBlob, gpu_compress, gpu_quantize, gpu_row_lsq, gpu_row_sumsq, log
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [S.BF16, S.FP16, S.FP8, S.INT8]
+
+
+def weights(dtype, R, C, seed):
+    if dtype == S.FP16:
+        return S.student_t_outliers(R, C, seed=seed)
+    if dtype == S.FP8:
+        return S.laplace_pair(R, C, seed=seed)[1]
+    if dtype == S.INT8:
+        return S.laplace_pair(R, C, seed=seed)[2]
+    return S.lognormal_rows(R, C, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(64, 64), (130, 200), (7, 1032)])
+def test_row_sumsq(orc, dtype, shape):
+    log("row_sumsq", dtype, shape)
+    w = weights(dtype, *shape, seed=11)
+    got = gpu_row_sumsq(w, dtype)
+    ref = orc.row_sumsq(w, dtype)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("s", [0.03, 0.4, 2.5])
+def test_quantize_and_histogram(orc, dtype, s):
+    log("quantize", dtype, s)
+    w = weights(dtype, 96, 264, seed=5)
+    ss = orc.row_sumsq(w, dtype)
+    g = orc.gains(ss, w.shape[1], s)
+    err, cos, fld, hist = gpu_quantize(w, dtype, g)
+    st, cos_o, fld_o = orc.quantize(w, dtype, g)
+    assert (err != 0) == (st != 0)
+    if st == 0:
+        assert np.array_equal(cos, cos_o)
+        assert np.array_equal(fld, fld_o)
+        assert np.array_equal(hist.astype(np.uint64), orc.histogram(cos_o, fld_o))
+    else:
+        assert err & (1 << 5)
+
+
+def test_quantize_row_selection(orc):
+    log("quantize row selection")
+    w = S.lognormal_rows(300, 512, seed=3)
+    ss = orc.row_sumsq(w, S.BF16)
+    sel = np.array([(i * 300) // 256 for i in range(256)], np.int64)
+    g = np.zeros(300, np.float32)
+    g[sel] = orc.gains(ss[sel], 512, 0.3)
+    err, cos, fld, hist = gpu_quantize(w, S.BF16, g, row_sel=sel)
+    st, cos_o, fld_o = orc.quantize(w, S.BF16, g, row_sel=sel)
+    assert err == 0 and st == 0
+    assert np.array_equal(cos, cos_o) and np.array_equal(fld, fld_o)
+    assert np.array_equal(hist.astype(np.uint64), orc.histogram(cos_o, fld_o))
+
+
+def test_quantize_range_error(orc):
+    log("quantize range")
+    w = S.iid_normal(8, 64, seed=2)
+    ss = orc.row_sumsq(w, S.BF16)
+    g = orc.gains(ss, 64, 1e-6)
+    err, *_ = gpu_quantize(w, S.BF16, g)
+    assert err & (1 << 5)
+    assert orc.quantize(w, S.BF16, g)[0] == orc.ERR_RANGE
+
+
+def test_quantize_special_vectors(orc):
+    """Hand-worked E8 cases (tests/golden/e8_cases.txt) through the GPU quantiser with unit gain:
+    cases that bf16 holds exactly must give the worked answer; all must match the oracle."""
+    from test_oracle_e8 import golden_cases
+
+    log("quantize golden")
+    cases = golden_cases()
+    x = np.stack([c[0] for c in cases]).astype(np.float32)
+    bits = S.cast_container(x, S.BF16)
+    exact = np.all(S.container_to_float(bits, S.BF16) == x, axis=1)
+    w = np.ascontiguousarray(bits.reshape(len(cases), 8))
+    g = np.ones(len(cases), np.float32)
+    err, cos, fld, _ = gpu_quantize(w, S.BF16, g)
+    st, cos_o, fld_o = orc.quantize(w, S.BF16, g)
+    assert err == 0 and st == 0
+    assert np.array_equal(cos, cos_o) and np.array_equal(fld, fld_o)
+    assert exact.sum() >= 5
+    for i, c in enumerate(cases):
+        if exact[i]:
+            assert cos[i] == c[1], c[4]
+            assert np.array_equal(fld[8 * i:8 * i + 8], c[3]), c[4]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_row_lsq(orc, dtype):
+    log("row_lsq", dtype)
+    w = weights(dtype, 70, 392, seed=8)
+    ss = orc.row_sumsq(w, dtype)
+    g = orc.gains(ss, 392, 0.5)
+    st, cos, fld = orc.quantize(w, dtype, g)
+    assert st == 0
+    num, den4 = gpu_row_lsq(w, dtype, cos, fld)
+    num_o, den4_o = orc.row_lsq(w, dtype, cos, fld)
+    assert np.array_equal(num.view(np.uint64), num_o.view(np.uint64))
+    assert np.array_equal(den4, den4_o)
+
+
+# (key, rows, cols) -- reduced shapes of the five workloads, several tiles each; the ragged
+# cases leave a partial last tile.
+DECODE_CASES = [
+    (1, 256, 256),          # 16 tiles of 512 vectors, J = 8
+    (2, 512, 1024),         # J = 16
+    (2, 200, 776),          # ragged: 19400 vectors, last tile 968 of 1024
+    (3, 256, 1024),         # fp16, heavy tails: wide-alphabet path
+    (4, 96, 3072),          # J = 16, tiles span rows
+    ("5a", 64, 2048),       # fp8, J = 32
+    ("5b", 64, 2048),       # int8, J = 32, wide alphabet
+    ("5b", 37, 1000),       # ragged J = 32, 3 tiles
+    (1, 3, 8),              # one vector per row, single ragged tile
+]
+
+
+def _oracle_blob(orc, key, R, C, target=None):
+    wl = S.WORKLOADS[key]
+    w = S.workload_weights(key, R, C)
+    st, blob, s = orc.compress(w, wl["dtype"], target or wl["target_bpp"], wl["tile_fields"])
+    assert st == 0
+    return w, blob
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_decode_matches_oracle(orc, case):
+    key, R, C = case
+    log("decode", case)
+    w, blob = _oracle_blob(orc, key, R, C)
+    gb = GpuBlob(blob)
+    err, out = gb.decode()
+    st, ref, _, _ = orc.decompress(blob)
+    assert st == 0 and err == 0
+    assert out.shape == ref.shape and out.dtype == ref.dtype
+    assert np.array_equal(out, ref)
+    # determinism: a second launch gives the same bytes
+    err2, out2 = gb.decode()
+    assert err2 == 0 and np.array_equal(out2, out)
+
+
+@pytest.mark.parametrize("target", [0.001, 1.0, 8.0, 11.0])
+def test_decode_extreme_rates(orc, target):
+    log("decode rate", target)
+    w, blob = _oracle_blob(orc, 2, 128, 1024, target=target)
+    err, out = GpuBlob(blob).decode()
+    st, ref, _, _ = orc.decompress(blob)
+    assert err == 0 and np.array_equal(out, ref)
+
+
+def test_decode_zero_matrix(orc):
+    log("decode zeros")
+    z = np.zeros((64, 512), np.uint16)
+    st, blob, s = orc.compress(z, S.BF16, 3.0, 4096)
+    err, out = GpuBlob(blob).decode()
+    assert err == 0 and np.all(out == 0)
+
+
+def test_decode_detects_corrupt_tile(orc):
+    log("decode corrupt")
+    w, blob = _oracle_blob(orc, 2, 256, 1024)
+    info = orc.blob_fields(blob)
+    bad = blob.copy()
+    bad[-64] ^= 0x5A                                  # a payload word of the last tile
+    gb = GpuBlob(bad)
+    err, _ = gb.decode()
+    assert err & (1 << 7)
+    assert orc.decompress(bad)[0] == orc.ERR_CORRUPT
+    assert info["tiles"] > 1
+
+
+@pytest.mark.parametrize("case", [(1, 256, 256), (2, 256, 1024), (3, 128, 1024),
+                                  ("5a", 32, 2048), ("5b", 32, 2048), (2, 200, 776)],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_compress_blob_matches_oracle(orc, case):
+    """The library's compress (GPU quantiser, histogram, row sums and LS terms; host tables,
+    encoder and search) writes the oracle's blob byte for byte."""
+    key, R, C = case
+    log("compress", case)
+    wl = S.WORKLOADS[key]
+    w = S.workload_weights(key, R, C)
+    blob, s = gpu_compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"])
+    st, blob_o, s_o = orc.compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"])
+    assert st == 0
+    assert s == s_o
+    assert blob.size == blob_o.size and np.array_equal(blob, blob_o)
+
+
+def test_high_level_roundtrip(orc):
+    """The usage of the design page: compress at 3.5 bpp, decompress, same shape and dtype."""
+    import torch
+
+    import entropy_coded_weight_ep_amd as ep
+
+    log("high level")
+    w = S.workload_weights(1)
+    t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    cfg = ep.LatticeRANSConfig(target_bpp=3.5, tile_fields=4096)
+    c = ep.compress(t, cfg)
+    r = ep.decompress(c, cfg)
+    assert r.shape == t.shape and r.dtype == t.dtype
+    rel = ((r.float() - t.float()).norm() / t.float().norm()).item()
+    assert 0.0 < rel < 0.3
+    assert abs(c.actual_bpp - 8.0 * c.blob.size / w.size) < 1e-12
+    st, blob_o, _ = orc.compress(w, S.BF16, 3.5, 4096)
+    assert np.array_equal(c.blob, blob_o)
