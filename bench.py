@@ -8,6 +8,8 @@ matrix (one kernel launch).  Eight copies of blob + output are rotated so the wo
 
 Also timed in the same run: the E8 quantiser + histogram kernel on the same matrix (the
 encoder's GPU hot path), and the CPU oracle's decode (single thread) as a baseline.
+--workload selects one of the other synthetic workloads (3, 4, 5a, 5b, 1) for the same
+measurement; the default line is the 4096 x 4096 one.
 
 Prints one JSON line.
 """
@@ -35,6 +37,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="2",
+                    help="workload key: 2 (default, the headline line), 3, 4, 5a, 5b, 1")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decoder shards tiles with no exchange, and no "
@@ -47,12 +53,17 @@ def main():
     import entropy_coded_weight_ep_amd as ep
     import ep_synth as S
 
-    wl = S.WORKLOADS[2]
+    key = int(args.workload) if args.workload.isdigit() else args.workload
+    wl = S.WORKLOADS[key]
     R, C, F, target = wl["rows"], wl["cols"], wl["tile_fields"], wl["target_bpp"]
+    dt = wl["dtype"]
+    esize = S.ELEM_SIZE[dt]
+    tdt = {S.BF16: torch.bfloat16, S.FP16: torch.float16, S.FP8: torch.float8_e4m3fn,
+           S.INT8: torch.int8}[dt]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w_bits = S.workload_weights(2)
-    t = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w_bits = S.workload_weights(key)
+    t = torch.from_numpy(w_bits.view(np.uint8)).to(dev).view(tdt).view(R, C)
 
     # compress once (library: GPU rate search, quantiser, histogram, LS scales; host encoder)
     t0 = time.time()
@@ -60,7 +71,7 @@ def main():
     compress_s = time.time() - t0
     info = comp.info
     blob_bytes = int(comp.blob.size)
-    out_bytes = R * C * 2
+    out_bytes = R * C * esize
 
     # rotated copies of blob, decode tables and outputs
     blobs, tabs, outs = [], [], []
@@ -70,7 +81,7 @@ def main():
         assert ep.ep_prepare_decode(d, info, tb) == 0
         blobs.append(d)
         tabs.append(tb)
-        outs.append(torch.empty((R, C), dtype=torch.bfloat16, device=dev))
+        outs.append(torch.empty((R, C), dtype=tdt, device=dev))
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
@@ -99,7 +110,7 @@ def main():
 
     # E8 quantiser + histogram on the same matrix at the selected scale (gains from the blob's s)
     sumsq = torch.empty(R, dtype=torch.float64, device=dev)
-    assert ep.ep_row_sumsq(t, ep.EP_BF16, R, C, sumsq) == 0
+    assert ep.ep_row_sumsq(t, dt, R, C, sumsq) == 0
     rms = torch.sqrt(sumsq / C)
     gains = torch.where(rms > 0, 1.0 / (rms * comp.scale), torch.zeros_like(rms)).float()
     cos = torch.empty(R * C // 8, dtype=torch.uint8, device=dev)
@@ -108,19 +119,28 @@ def main():
     qerr = torch.zeros(1, dtype=torch.int32, device=dev)
     qsteps = max(10, args.steps // 4)
     for _ in range(3):
-        ep.ep_quantize_e8(t, ep.EP_BF16, R, C, gains, None, R, cos, fld, hist, qerr)
+        ep.ep_quantize_e8(t, dt, R, C, gains, None, R, cos, fld, hist, qerr)
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(qsteps):
-        ep.ep_quantize_e8(t, ep.EP_BF16, R, C, gains, None, R, cos, fld, hist, qerr)
+        ep.ep_quantize_e8(t, dt, R, C, gains, None, R, cos, fld, hist, qerr)
     ev1.record()
     torch.cuda.synchronize()
     q_ms = ev0.elapsed_time(ev1) / qsteps
-    q_bytes = R * C * 2 + R * C // 8 + R * C * 2        # read weights, write cosets + fields
+    q_bytes = R * C * esize + R * C // 8 + R * C * 2    # read weights, write cosets + fields
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     value = out_bytes / (ms * 1e-3) / 1e9
     algo_bytes = blob_bytes + out_bytes
     achieved = algo_bytes / (ms * 1e-3) / 1e9
+    J = F // 512
+    kname = f"k_decode<{J}, {S.DTYPE_NAMES[dt]}>"
     line = {
         "metric": "decoded weight GB/s/GPU (output bytes) + % of HBM roofline; actual_bpp",
         "value": round(value, 2),
@@ -135,9 +155,9 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {
-            "workload": "4096x4096 bf16, log-normal row scales (mu=log 0.02, sigma=0.5), "
-                        "target 4.0 bpp, 8192-field tiles, one fused decode per step",
-            "rows": R, "cols": C, "container": "bf16", "tile_fields": F,
+            "workload": wl["name"] + f", target {target} bpp, {F}-field tiles, "
+                        "one fused decode per step",
+            "rows": R, "cols": C, "container": S.DTYPE_NAMES[dt], "tile_fields": F,
             "target_bpp": target, "actual_bpp": round(info.actual_bpp, 5),
             "scale": comp.scale, "rel_l2": round(rel_l2, 6),
             "blob_bytes": blob_bytes, "output_bytes": out_bytes,
@@ -145,12 +165,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_decode<16, bf16>",
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(kname, str(key)),
+            "kernel": kname,
             "bytes_per_launch": algo_bytes,
         },
         "quantize": {
-            "kernel": "k_quantize_e8<bf16> + histogram",
+            "kernel": f"k_quantize_e8<{S.DTYPE_NAMES[dt]}> + histogram",
             "ms": round(q_ms, 6), "bytes_per_launch": q_bytes,
             "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
             "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -159,6 +180,29 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(comp.blob, out_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def decoder_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "entropy_coded_weight_ep_amd", "csrc")
+    for f in ("ep_decode.h", "ep_device.h", "ep_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy of known size), or None when no summary exists for this
+    kernel and workload or the decoder sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("decoder_source_sha") != decoder_source_sha():
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(blob, out_bytes, min_seconds):

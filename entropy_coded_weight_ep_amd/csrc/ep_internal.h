@@ -14,7 +14,8 @@ struct TableArgs {
   int32_t lo[EP_NTABLES];
 };
 
-// Wavefronts (= tiles) per decoder workgroup.
+// Largest number of wavefronts (= tiles) per decoder workgroup; the launcher uses 8, 4, 2 or 1,
+// the most whose LDS (tables + per-wave words) fits in a CU.
 constexpr int kDecWaves = 8;
 
 // Kernel arguments of the fused tile decoder.
@@ -35,7 +36,7 @@ struct DecodeArgs {
 
 // Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).
 template <int DT>
-hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, size_t lds,
-                         hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, int waves,
+                         size_t lds, hipStream_t s);
 
 }  // namespace ep

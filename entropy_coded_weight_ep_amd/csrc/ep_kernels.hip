@@ -439,9 +439,11 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
   for (int t = 0; t < EP_NTABLES; t++) a.lo[t] = info->lo[t];
   a.coset_f0 = info->coset_freq0;
   const bool big = info->big_alphabet != 0;
-  const size_t lds = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0) +
-                     (size_t)kDecWaves * a.words_stride * 2;
-  if (lds > 160 * 1024) return EP_ERR_VERSION;
+  const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
+  int waves = kDecWaves;
+  while (waves > 1 && lds_tables + (size_t)waves * a.words_stride * 2 > 160 * 1024) waves >>= 1;
+  const size_t lds = lds_tables + (size_t)waves * a.words_stride * 2;
+  if (lds > 160 * 1024) return EP_ERR_VERSION;      // one tile's words do not fit in LDS
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t tiles = (uint32_t)info->tiles;
   const uint32_t V = (uint32_t)info->tile_fields / 8;
@@ -451,10 +453,10 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
     a.tile_begin = t0;
     a.tile_end = t1;
     switch (info->dtype) {
-      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, lds, s);
-      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, lds, s);
-      case EP_FP8_E4M3FN: return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, lds, s);
-      default: return launch_decode<EP_INT8>(a, J, big, ragged, lds, s);
+      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, waves, lds, s);
+      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, waves, lds, s);
+      case EP_FP8_E4M3FN: return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, waves, lds, s);
+      default: return launch_decode<EP_INT8>(a, J, big, ragged, waves, lds, s);
     }
   };
   if (full_tiles > 0 && launch(0, full_tiles, false) != hipSuccess) return EP_ERR_HIP;

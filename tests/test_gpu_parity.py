@@ -221,3 +221,42 @@ def test_high_level_roundtrip(orc):
     assert abs(c.actual_bpp - 8.0 * c.blob.size / w.size) < 1e-12
     st, blob_o, _ = orc.compress(w, S.BF16, 3.5, 4096)
     assert np.array_equal(c.blob, blob_o)
+
+
+def _midpoint_alphas(n, seed):
+    """fp32 row scales a for which fp16(fp32(a * p)) differs from a single rounding of the exact
+    product a * p for some half-integer p in [-32, 32]: the products land on fp16 midpoints only
+    after the fp32 rounding.  The decoder must round twice (fp32, then the container)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    p = np.arange(-64, 65, dtype=np.float64) / 2
+    out = []
+    while len(out) < n:
+        a = np.float32(g.uniform(0.004, 0.06))
+        y32 = (a * p.astype(np.float32)).astype(np.float32)
+        if np.any(y32.astype(np.float16) != (float(a) * p).astype(np.float16)):
+            out.append(a)
+    return np.array(out, np.float32)
+
+
+def test_decode_double_rounding_midpoints(orc):
+    """Row scales chosen so that many fp32 products sit on fp16 rounding midpoints."""
+    log("decode midpoints")
+    w, blob = _oracle_blob(orc, 3, 64, 1024)
+    info = orc.blob_fields(blob)
+    o = 64 + info["table_bytes"]
+    bad = blob.copy()
+    alphas = _midpoint_alphas(64, seed=17)
+    bad[o:o + 4 * 64] = alphas.view(np.uint8)
+    st, ref, cos, fld = orc.decompress(bad, want_fields=True)
+    assert st == 0
+    # how many elements would a single rounding get wrong?
+    z = fld.reshape(-1, 8).astype(np.int64)
+    z[:, 7] = 2 * z[:, 7] + (z[:, :7].sum(axis=1) & 1)
+    p = (z + 0.5 * cos[:, None]).reshape(64, 1024)
+    y32 = (alphas[:, None] * p.astype(np.float32)).astype(np.float32)
+    single = (alphas[:, None].astype(np.float64) * p).astype(np.float16)
+    n_mid = int(np.sum(y32.astype(np.float16) != single))
+    assert n_mid > 10
+    err, out = GpuBlob(bad).decode()
+    assert err == 0
+    assert np.array_equal(out, ref), f"{int(np.sum(out != ref))} elements differ"
