@@ -26,6 +26,8 @@ FLAGS = [
     "-ffp-contract=off",
     # packed fp32 VALU forms are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the decoder's phase loop must unroll fully (its fields live in registers indexed by phase)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -40,52 +40,13 @@ __device__ __forceinline__ float widen(uint32_t bits) {
   }
 }
 
-// fp32 -> E4M3FN, round to nearest even, saturating at +-448 (NaN -> 0x7F).
-__device__ __forceinline__ uint32_t f32_to_fp8e4m3(float y) {
-  uint32_t u = __float_as_uint(y);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = __builtin_fabsf(y);
-  uint32_t code;
-  if (a != a) {
-    code = 0x7Fu;
-  } else if (a >= 448.0f) {
-    code = 0x7Eu;                                                  // saturate
-  } else if (a < 0.015625f) {                                      // below 2^-6: subnormal step
-    code = (uint32_t)__builtin_rintf(a * 512.0f);                  // 8 -> smallest normal
-  } else {
-    uint32_t ua = __float_as_uint(a);
-    uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);                // RNE to 3 mantissa bits
-    code = (r >> 20) - (120u << 3);
-  }
-  return sign | code;
-}
-
+// fp32 -> bf16 / fp16, round to nearest even (hardware conversions; fp16 overflow -> inf).
 template <int DT>
 __device__ __forceinline__ uint32_t narrow(float y) {
-  if constexpr (DT == EP_BF16) {
-    return __builtin_bit_cast(uint16_t, (__bf16)y);
-  } else if constexpr (DT == EP_FP16) {
-    return __builtin_bit_cast(uint16_t, (_Float16)y);
-  } else if constexpr (DT == EP_FP8_E4M3FN) {
-    return f32_to_fp8e4m3(y);
-  } else {
-    float r = __builtin_rintf(y);
-    r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
-    int32_t q = (y != y) ? 0 : (int32_t)r;
-    return (uint32_t)(uint8_t)(int8_t)q;
-  }
+  static_assert(DT == EP_BF16 || DT == EP_FP16, "fp8 and int8 are converted in the decoder");
+  if constexpr (DT == EP_BF16) return __builtin_bit_cast(uint16_t, (__bf16)y);
+  else return __builtin_bit_cast(uint16_t, (_Float16)y);
 }
-
-template <int DT>
-struct Elem8;  // eight consecutive container elements
-template <>
-struct Elem8<EP_BF16> { using V = uint4; };
-template <>
-struct Elem8<EP_FP16> { using V = uint4; };
-template <>
-struct Elem8<EP_FP8_E4M3FN> { using V = uint2; };
-template <>
-struct Elem8<EP_INT8> { using V = uint2; };
 
 template <int DT>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float out[8]) {

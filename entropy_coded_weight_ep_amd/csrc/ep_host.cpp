@@ -401,6 +401,12 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
     p += record_bytes(n);
   }
   if (round16(p - L.tables) != (int64_t)tb) return EP_ERR_CORRUPT;
+  // row scales must be finite (the decoder's saturating conversions assume it)
+  for (int64_t r = 0; r < I.rows; r++) {
+    float alpha;
+    std::memcpy(&alpha, b + L.alpha + 4 * r, 4);
+    if (!std::isfinite(alpha)) return EP_ERR_CORRUPT;
+  }
   const uint32_t* off = reinterpret_cast<const uint32_t*>(b + L.word_off);
   if (off[0] != 0 || (int64_t)off[I.tiles] != I.payload_words) return EP_ERR_CORRUPT;
   uint32_t maxw = 0;

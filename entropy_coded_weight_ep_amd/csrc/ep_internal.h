@@ -14,9 +14,12 @@ struct TableArgs {
   int32_t lo[EP_NTABLES];
 };
 
-// Largest number of wavefronts (= tiles) per decoder workgroup; the launcher uses 8, 4, 2 or 1,
-// the most whose LDS (tables + per-wave words) fits in a CU.
-constexpr int kDecWaves = 8;
+// Largest number of wavefronts (= tiles) per decoder workgroup (16 for up to 16 vectors per
+// lane, 8 for 32); the launcher picks 16, 8, 4, 2 or 1 from LDS, registers and the tile count.
+constexpr int kDecWaves = 16;
+// Compute units of an MI355X and LDS bytes per CU, for the decoder's workgroup size choice.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kLdsPerCU = 160 * 1024;
 
 // Kernel arguments of the fused tile decoder.
 struct DecodeArgs {
@@ -24,13 +27,14 @@ struct DecodeArgs {
   const uint32_t* word_off;   // u32[tiles + 1]
   const uint32_t* states;     // u32[tiles][64]
   const uint16_t* words;      // u16[payload words], 16-byte aligned section
-  const uint32_t* ent;        // expanded field tables: u32[16][4096]
+  const uint32_t* ent;        // slot entries f | (slot - cum) << 13 | value << 25: u32[16][4096]
   const int16_t* val;         // field value per slot: i16[16][4096]
   void* out;                  // container[rows][cols]
   uint32_t* err;              // device error word
   uint32_t tile_begin, tile_end;  // tiles decoded by this launch
   uint32_t n_vec, vpr, max_tile_words, words_stride, coset_f0;
-  double inv_vpr;
+  double inv_vpr;             // 1 / vectors per row
+  float inv_vpr_f;
   int32_t lo[EP_NTABLES];
 };
 

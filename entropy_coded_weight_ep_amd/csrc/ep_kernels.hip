@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ep.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -270,8 +272,8 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 // ------------------------------------------------------------------------------------------
 // Decode-table expansion (once per blob).  For each of the 16 field tables, slot s of [0, 2^P)
 // belongs to the value v with cum(v) <= s < cum(v) + f(v) and gets
-//   entry = f | (s - cum) << 13 | (v & 127) << 25        (32 bits)
-//   value = v                                             (int16, used for wide alphabets)
+//   entry = f(v) | (s - cum(v)) << 13 | (v & 127) << 25        (u32)
+//   value = v                                                   (i16, for wide alphabets)
 // The 7-bit value in the entry is exact whenever every field value lies in [-64, 63].
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict__ blob,
@@ -401,9 +403,9 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
     ta.lo[t] = info->lo[t];
   }
   uint32_t* ent = static_cast<uint32_t*>(d_dec_tables);
-  int16_t* sym = reinterpret_cast<int16_t*>(ent + 16 * kM);
+  int16_t* val = reinterpret_cast<int16_t*>(ent + 16 * kM);
   k_expand_tables<<<16, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(d_blob), ta, ent, sym);
+      static_cast<const uint8_t*>(d_blob), ta, ent, val);
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -433,17 +435,33 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
   a.n_vec = (uint32_t)nv;
   a.vpr = (uint32_t)(info->cols / 8);
   a.inv_vpr = 1.0 / (double)a.vpr;
+  a.inv_vpr_f = 1.0f / (float)a.vpr;
   a.max_tile_words = info->max_tile_words;
   // words region per wave: the aligned chunks of the largest tile plus one wave of slack
   a.words_stride = ((info->max_tile_words + 7u + 7u) & ~7u) + 64u;
   for (int t = 0; t < EP_NTABLES; t++) a.lo[t] = info->lo[t];
   a.coset_f0 = info->coset_freq0;
+  // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
+  // per wave 256 B of states and the words region.  Waves per workgroup (8, 4, 2 or 1): the
+  // choice that keeps the most tiles resident at once, preferring more waves on ties.
   const bool big = info->big_alphabet != 0;
   const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
-  int waves = kDecWaves;
-  while (waves > 1 && lds_tables + (size_t)waves * a.words_stride * 2 > 160 * 1024) waves >>= 1;
-  const size_t lds = lds_tables + (size_t)waves * a.words_stride * 2;
-  if (lds > 160 * 1024) return EP_ERR_VERSION;      // one tile's words do not fit in LDS
+  auto lds_of = [&](int w) { return lds_tables + (size_t)w * (256 + (size_t)a.words_stride * 2); };
+  // waves per SIMD the decoder's registers allow: 8, 4 and 2 for 8, 16 and 32 vectors per lane
+  const int64_t waves_per_cu = 4 * (J <= 8 ? 8 : (J <= 16 ? 4 : 2));
+  const int max_waves = J <= 16 ? kDecWaves : kDecWaves / 2;
+  int waves = 0;
+  int64_t best = -1;
+  for (int w = max_waves; w >= 1; w >>= 1) {
+    if ((int64_t)lds_of(w) > kLdsPerCU) continue;
+    const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w), waves_per_cu / w);
+    const int64_t grid = (info->tiles + w - 1) / w;
+    const int64_t resident = std::min(grid, kCUs * per_cu) * w;
+    // most tiles in flight; on a tie, the smaller workgroup (spread over more CUs)
+    if (resident >= best) { best = resident; waves = w; }
+  }
+  if (waves == 0) return EP_ERR_VERSION;             // one tile's words do not fit in LDS
+  const size_t lds = lds_of(waves);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t tiles = (uint32_t)info->tiles;
   const uint32_t V = (uint32_t)info->tile_fields / 8;

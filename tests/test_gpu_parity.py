@@ -260,3 +260,37 @@ def test_decode_double_rounding_midpoints(orc):
     err, out = GpuBlob(bad).decode()
     assert err == 0
     assert np.array_equal(out, ref), f"{int(np.sum(out != ref))} elements differ"
+
+
+@pytest.mark.parametrize("key,shape", [(2, (64, 1024)), (3, (64, 1024)), ("5a", (32, 2048)),
+                                       ("5b", (32, 2048))], ids=lambda c: str(c))
+def test_decode_container_edges(orc, key, shape):
+    """Row scales swept over 1e-40 .. 1e4 with both signs, so that the decoded products reach
+    container subnormals, saturation (fp8 at +-448, int8 at -128 / 127) and overflow (fp16 to
+    +-inf); the GPU conversions must match the oracle's bit for bit."""
+    R, C = shape
+    log("decode edges", key)
+    w, blob = _oracle_blob(orc, key, R, C)
+    info = orc.blob_fields(blob)
+    o = 64 + info["table_bytes"]
+    g = np.random.Generator(np.random.PCG64(23))
+    alphas = (10.0 ** np.linspace(-40, 4, R) * np.where(g.random(R) < 0.5, -1.0, 1.0))
+    alphas = alphas.astype(np.float32)
+    bad = blob.copy()
+    bad[o:o + 4 * R] = alphas.view(np.uint8)
+    st, ref, _, _ = orc.decompress(bad)
+    assert st == 0
+    err, out = GpuBlob(bad).decode()
+    assert err == 0
+    assert np.array_equal(out, ref), f"{int(np.sum(out != ref))} elements differ"
+
+
+def test_blob_with_nonfinite_scale_is_rejected(orc):
+    import entropy_coded_weight_ep_amd as ep
+
+    w, blob = _oracle_blob(orc, 1, 64, 256)
+    info = orc.blob_fields(blob)
+    o = 64 + info["table_bytes"]
+    bad = blob.copy()
+    bad[o:o + 4] = np.array([np.inf], np.float32).view(np.uint8)
+    assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_CORRUPT
