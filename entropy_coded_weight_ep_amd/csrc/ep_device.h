@@ -48,6 +48,21 @@ __device__ __forceinline__ uint32_t narrow(float y) {
   else return __builtin_bit_cast(uint16_t, (_Float16)y);
 }
 
+// Two fp32 values -> packed pair (low half: a), round to nearest even: one packed conversion.
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+  static_assert(DT == EP_BF16 || DT == EP_FP16, "16-bit containers only");
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  if constexpr (DT == EP_BF16) {
+    typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2));
+  } else {
+    typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h16x2));
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float out[8]) {
   if constexpr (DT == EP_BF16 || DT == EP_FP16) {

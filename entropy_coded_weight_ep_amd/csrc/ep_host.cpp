@@ -401,11 +401,14 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
     p += record_bytes(n);
   }
   if (round16(p - L.tables) != (int64_t)tb) return EP_ERR_CORRUPT;
-  // row scales must be finite (the decoder's saturating conversions assume it)
+  // row scales must be finite (the decoder's saturating conversions assume it); a nonzero scale
+  // below 2^-125 in magnitude has an inexact half, which the decoder's fused scaling needs exact
+  bool tiny = false;
   for (int64_t r = 0; r < I.rows; r++) {
     float alpha;
     std::memcpy(&alpha, b + L.alpha + 4 * r, 4);
     if (!std::isfinite(alpha)) return EP_ERR_CORRUPT;
+    tiny |= alpha != 0.0f && std::fabs(alpha) < 0x1p-125f;
   }
   const uint32_t* off = reinterpret_cast<const uint32_t*>(b + L.word_off);
   if (off[0] != 0 || (int64_t)off[I.tiles] != I.payload_words) return EP_ERR_CORRUPT;
@@ -416,6 +419,7 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   }
   if (maxw != I.max_tile_words) return EP_ERR_CORRUPT;
   I.big_alphabet = big ? 1u : 0u;
+  I.tiny_scale = tiny ? 1u : 0u;
   I.bytes = (int64_t)bytes;
   I.actual_bpp = 8.0 * (double)bytes / ((double)I.rows * (double)I.cols);
   I.off_tables = L.tables;

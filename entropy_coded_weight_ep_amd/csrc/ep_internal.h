@@ -39,8 +39,9 @@ struct DecodeArgs {
 };
 
 // Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).
+// `slow`: scale without the fused multiply-add (needed for bf16 when some row scale is tiny).
 template <int DT>
-hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, int waves,
+hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, int waves,
                          size_t lds, hipStream_t s);
 
 }  // namespace ep

@@ -467,14 +467,18 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
   const uint32_t V = (uint32_t)info->tile_fields / 8;
   const bool last_ragged = (uint64_t)tiles * V != (uint64_t)nv;
   const uint32_t full_tiles = last_ragged ? tiles - 1 : tiles;
+  // the fused scaling is exact for fp16, fp8 and int8 whatever the scales (a tiny scale's products
+  // round to zero in those containers); bf16 keeps the subnormal range and needs the exact half
+  const bool slow = info->tiny_scale != 0;
   auto launch = [&](uint32_t t0, uint32_t t1, bool ragged) -> hipError_t {
     a.tile_begin = t0;
     a.tile_end = t1;
     switch (info->dtype) {
-      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, waves, lds, s);
-      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, waves, lds, s);
-      case EP_FP8_E4M3FN: return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, waves, lds, s);
-      default: return launch_decode<EP_INT8>(a, J, big, ragged, waves, lds, s);
+      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, slow, waves, lds, s);
+      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, false, waves, lds, s);
+      case EP_FP8_E4M3FN:
+        return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, waves, lds, s);
+      default: return launch_decode<EP_INT8>(a, J, big, ragged, false, waves, lds, s);
     }
   };
   if (full_tiles > 0 && launch(0, full_tiles, false) != hipSuccess) return EP_ERR_HIP;
