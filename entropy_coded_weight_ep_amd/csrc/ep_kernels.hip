@@ -117,92 +117,177 @@ __device__ __forceinline__ int e8_nearest(const float x[8], int32_t z[8]) {
   return c;
 }
 
-// Histogram privatisation window in LDS: values [-128, 127] of every table.
-constexpr int kHistWin = 256;
-constexpr int kHistOff = 128;
+// Histogram privatisation window in LDS: values [-256, 255] of every table.  Tables are laid
+// out 514 counters apart, which puts the coset-1 table of a field 16 banks away from the coset-0
+// one: the most frequent bins of the two (values near 0) do not share an LDS bank.
+constexpr int kHistWin = 512;
+constexpr int kHistOff = 256;
+constexpr int kHistStride = 514;
 
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     p[i] = v;
 }
 
+// One vector's input, fetched one iteration ahead of its use: raw container bits (16 bytes for
+// 16-bit containers, 8 for 8-bit ones), the row gain, and whether the row index was valid.
+struct QIn {
+  uint4 raw;
+  float g;
+  bool ok;
+};
+
 template <int DT>
-__global__ __launch_bounds__(256) void k_quantize_e8(
+__device__ __forceinline__ QIn q_fetch(const void* __restrict__ w, int64_t rows, int64_t cols,
+                                       const float* __restrict__ gain,
+                                       const int64_t* __restrict__ row_index, uint32_t v,
+                                       uint32_t vpr, double inv_vpr) {
+  QIn q;
+  // i = v / vpr: fp64 estimate, then one exact correction
+  uint32_t i = (uint32_t)((double)v * inv_vpr);
+  const int64_t rem = (int64_t)v - (int64_t)i * vpr;
+  i = rem < 0 ? i - 1 : (rem >= (int64_t)vpr ? i + 1 : i);
+  const uint32_t m = v - i * vpr;
+  const int64_t r = row_index ? row_index[i] : (int64_t)i;
+  q.ok = r >= 0 && r < rows;
+  q.raw = make_uint4(0, 0, 0, 0);
+  q.g = 0.0f;
+  if (q.ok) {
+    const int64_t e = r * cols + 8 * (int64_t)m;
+    if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+      q.raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + e);
+    } else {
+      const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(w) + e);
+      q.raw.x = h.x;
+      q.raw.y = h.y;
+    }
+    q.g = gain[r];
+  }
+  return q;
+}
+
+template <int DT>
+__device__ __forceinline__ void q_widen(const uint4& raw, float x[8]) {
+  if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[2 * i] = widen<DT>(w4[i] & 0xFFFFu);
+      x[2 * i + 1] = widen<DT>(w4[i] >> 16);
+    }
+  } else {
+    const uint32_t w2[2] = {raw.x, raw.y};
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] = widen<DT>((w2[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  }
+}
+
+// E8 quantiser + fused per-(coset, field) histogram.  A workgroup of 16 wavefronts walks the
+// vectors with a grid stride, fetching the next vector's input before quantising the current
+// one.  The histogram is privatised per workgroup in LDS (values [-256, 255] of every table; the
+// rest go straight to the global counts) and merged once at the end; the coset table's two
+// counts are kept per lane.  Few, large workgroups keep the merge short, and each workgroup
+// starts its merge at a different bin so that they do not all hit the same global counters at
+// once.
+constexpr int kQThreads = 1024;
+
+template <int DT>
+__global__ __launch_bounds__(kQThreads) void k_quantize_e8(
     const void* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ gain,
-    const int64_t* __restrict__ row_index, uint32_t n_vec, uint32_t vpr,
+    const int64_t* __restrict__ row_index, uint32_t n_vec, uint32_t vpr, double inv_vpr,
     uint8_t* __restrict__ coset, int16_t* __restrict__ fields, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ err) {
-  __shared__ uint32_t sh[EP_NTABLES * kHistWin];
+  __shared__ uint32_t sh[EP_NTABLES * kHistStride];
   const bool do_hist = hist != nullptr;
   if (do_hist) {
-    for (int i = threadIdx.x; i < EP_NTABLES * kHistWin; i += 256) sh[i] = 0;
+    for (int i = threadIdx.x; i < EP_NTABLES * kHistStride; i += kQThreads) sh[i] = 0;
     __syncthreads();
   }
   bool bad = false, bad_row = false;
-  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < n_vec; v += gridDim.x * 256u) {
-    const uint32_t i = v / vpr;
-    const uint32_t m = v - i * vpr;
-    const int64_t r = row_index ? row_index[i] : (int64_t)i;
-    if (r < 0 || r >= rows) {                // a row index outside the tensor: skip, report
+  uint32_t n_c0 = 0, n_c1 = 0;
+  const uint32_t stride = gridDim.x * (uint32_t)kQThreads;
+  uint32_t v = blockIdx.x * (uint32_t)kQThreads + threadIdx.x;
+  QIn cur;
+  if (v < n_vec) cur = q_fetch<DT>(w, rows, cols, gain, row_index, v, vpr, inv_vpr);
+  for (; v < n_vec; v += stride) {
+    QIn nxt;
+    const bool more = v + stride < n_vec;         // (no overflow: n_vec + stride < 2^32)
+    if (more) nxt = q_fetch<DT>(w, rows, cols, gain, row_index, v + stride, vpr, inv_vpr);
+    if (!cur.ok) {                                // a row index outside the tensor: skip, report
       bad_row = true;
-      continue;
-    }
-    float x[8];
-    load8<DT>(w, r * cols + 8 * (int64_t)m, x);
-    const float g = gain[r];
-    bool out_of_range = false;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      x[k] = __fmul_rn(x[k], g);
-      out_of_range |= !(__builtin_fabsf(x[k]) <= 65536.0f);
-    }
-    if (out_of_range) {
-#pragma unroll
-      for (int k = 0; k < 8; k++) x[k] = 0.0f;
-    }
-    int32_t z[8];
-    int c = e8_nearest(x, z);
-#pragma unroll
-    for (int k = 0; k < 8; k++) out_of_range |= (z[k] > 32767) | (z[k] < -32767);
-    if (out_of_range) {                      // flagged; keep every field (and bin) in range
-      c = 0;
-#pragma unroll
-      for (int k = 0; k < 8; k++) z[k] = 0;
-    }
-    bad |= out_of_range;
-    int32_t f[8];
-#pragma unroll
-    for (int k = 0; k < 7; k++) f[k] = z[k];
-    f[7] = z[7] >> 1;                                   // arithmetic shift = floor(z7 / 2)
-    coset[v] = (uint8_t)c;
-    uint4 pk;
-    pk.x = (uint32_t)(f[0] & 0xFFFF) | ((uint32_t)f[1] << 16);
-    pk.y = (uint32_t)(f[2] & 0xFFFF) | ((uint32_t)f[3] << 16);
-    pk.z = (uint32_t)(f[4] & 0xFFFF) | ((uint32_t)f[5] << 16);
-    pk.w = (uint32_t)(f[6] & 0xFFFF) | ((uint32_t)f[7] << 16);
-    reinterpret_cast<uint4*>(fields)[v] = pk;
-    if (do_hist) {
-      atomicAdd(&sh[kHistOff + c], 1u);
+    } else {
+      float x[8];
+      q_widen<DT>(cur.raw, x);
+      bool out_of_range = false;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
-        const int t = 1 + 8 * c + k;
-        const int32_t val = f[k];
-        if (val >= -kHistOff && val < kHistWin - kHistOff)
-          atomicAdd(&sh[t * kHistWin + val + kHistOff], 1u);
-        else
-          atomicAdd(&hist[(int64_t)t * EP_HIST_BINS + (val + 32768)], 1u);
+        x[k] = __fmul_rn(x[k], cur.g);
+        out_of_range |= !(__builtin_fabsf(x[k]) <= 65536.0f);
+      }
+      if (out_of_range) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] = 0.0f;
+      }
+      int32_t z[8];
+      int c = e8_nearest(x, z);
+#pragma unroll
+      for (int k = 0; k < 8; k++) out_of_range |= (z[k] > 32767) | (z[k] < -32767);
+      if (out_of_range) {                         // flagged; keep every field (and bin) in range
+        c = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) z[k] = 0;
+      }
+      bad |= out_of_range;
+      int32_t f[8];
+#pragma unroll
+      for (int k = 0; k < 7; k++) f[k] = z[k];
+      f[7] = z[7] >> 1;                           // arithmetic shift = floor(z7 / 2)
+      coset[v] = (uint8_t)c;
+      uint4 pk;
+      pk.x = (uint32_t)(f[0] & 0xFFFF) | ((uint32_t)f[1] << 16);
+      pk.y = (uint32_t)(f[2] & 0xFFFF) | ((uint32_t)f[3] << 16);
+      pk.z = (uint32_t)(f[4] & 0xFFFF) | ((uint32_t)f[5] << 16);
+      pk.w = (uint32_t)(f[6] & 0xFFFF) | ((uint32_t)f[7] << 16);
+      reinterpret_cast<uint4*>(fields)[v] = pk;
+      if (do_hist) {
+        n_c1 += (uint32_t)c;
+        n_c0 += 1u - (uint32_t)c;
+        // bins of value 0 of this vector's coset tables (field k at + k * kHistStride)
+        uint32_t* const hc = sh + (1 + 8 * c) * kHistStride + kHistOff;
+        uint32_t orr = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) orr |= (uint32_t)(f[k] + kHistOff);
+        if (orr < (uint32_t)kHistWin) {           // every field inside the window: the usual case
+#pragma unroll
+          for (int k = 0; k < 8; k++) atomicAdd(&hc[k * kHistStride + f[k]], 1u);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            const int32_t val = f[k];
+            if ((uint32_t)(val + kHistOff) < (uint32_t)kHistWin)
+              atomicAdd(&hc[k * kHistStride + val], 1u);
+            else
+              atomicAdd(&hist[(int64_t)(1 + 8 * c + k) * EP_HIST_BINS + (val + 32768)], 1u);
+          }
+        }
       }
     }
+    cur = nxt;
   }
   if (bad) atomicOr(err, 1u << EP_ERR_RANGE);
   if (bad_row) atomicOr(err, 1u << EP_ERR_ARG);
   if (do_hist) {
+    if (n_c0) atomicAdd(&sh[kHistOff + 0], n_c0);
+    if (n_c1) atomicAdd(&sh[kHistOff + 1], n_c1);
     __syncthreads();
-    for (int i = threadIdx.x; i < EP_NTABLES * kHistWin; i += 256) {
+    constexpr int kBins = EP_NTABLES * kHistStride;
+    const int rot = (int)((blockIdx.x * 1031u) % (uint32_t)kBins);
+    for (int j = threadIdx.x; j < kBins; j += kQThreads) {
+      const int i = j + rot < kBins ? j + rot : j + rot - kBins;
       const uint32_t cnt = sh[i];
       if (cnt) {
-        const int t = i / kHistWin;
-        const int val = i % kHistWin - kHistOff;
+        const int t = i / kHistStride;
+        const int val = i % kHistStride - kHistOff;   // (the 2 padding counters stay 0)
         atomicAdd(&hist[(int64_t)t * EP_HIST_BINS + (val + 32768)], cnt);
       }
     }
@@ -358,12 +443,16 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
     k_fill_u32<<<1024, 256, 0, s>>>(hist, (int64_t)EP_NTABLES * EP_HIST_BINS, 0u);
   }
   if (nvec == 0) return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
-  int64_t blocks = (nvec + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  // two 16-wavefront workgroups per compute unit at most: enough waves in flight with the
+  // one-ahead fetch, and few per-workgroup histogram merges
+  int64_t blocks = (nvec + kQThreads - 1) / kQThreads;
+  if (blocks > 2 * kCUs) blocks = 2 * kCUs;
   const dim3 grid((unsigned)blocks);
   const uint32_t nv = (uint32_t)nvec, vpr = (uint32_t)(cols / 8);
-#define EP_Q(DT) k_quantize_e8<DT><<<grid, 256, 0, s>>>(d_w, rows, cols, d_row_gain, d_row_index, nv, \
-                                                        vpr, d_coset, d_fields, hist, d_err)
+  const double inv_vpr = 1.0 / (double)vpr;
+#define EP_Q(DT) k_quantize_e8<DT><<<grid, kQThreads, 0, s>>>(d_w, rows, cols, d_row_gain,    \
+                                                              d_row_index, nv, vpr, inv_vpr,  \
+                                                              d_coset, d_fields, hist, d_err)
   switch (dtype) {
     case EP_BF16: EP_Q(EP_BF16); break;
     case EP_FP16: EP_Q(EP_FP16); break;
