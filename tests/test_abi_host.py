@@ -132,6 +132,23 @@ def test_blob_parse_rejects_corruption(ep, orc):
     assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_DTYPE
 
 
+@pytest.mark.parametrize("alpha,tiny", [(1e-40, 1), (-1e-40, 1), (0.0, 0), (-0.0, 0),
+                                         (2.0 ** -125, 0), (-(2.0 ** -125), 0),
+                                         (np.nextafter(np.float32(2.0 ** -125), np.float32(0)), 1),
+                                         (1.5, 0)])
+def test_blob_parse_flags_tiny_scales(ep, orc, alpha, tiny):
+    # a nonzero row scale below 2^-125 in magnitude has an inexact half: the parse flags it so
+    # that the decoder scales such blobs without the fused multiply-add
+    w = S.workload_weights(1)
+    st, blob, s = orc.compress(w, S.BF16, 3.5, 4096)
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0 and info.tiny_scale == 0
+    b = blob.copy()
+    b[info.off_alpha + 4 * 7:info.off_alpha + 4 * 8] = np.array([alpha], np.float32).view(np.uint8)
+    st, info2 = ep.ep_blob_parse(b)
+    assert st == 0 and info2.tiny_scale == tiny
+
+
 @pytest.mark.parametrize("s", [0.05, 0.3, 1.0, 4.0])
 def test_estimate_matches_oracle(ep, orc, s):
     w = S.lognormal_rows(600, 512, seed=4)
