@@ -32,7 +32,8 @@ struct DecodeArgs {
   void* out;                  // container[rows][cols]
   uint32_t* err;              // device error word
   uint32_t tile_begin, tile_end;  // tiles decoded by this launch
-  uint32_t n_vec, vpr, max_tile_words, words_stride, coset_f0;
+  uint32_t n_vec, vpr, max_tile_words, coset_f0;
+  uint32_t words_stride;       // words per wave region: the largest tile + slack, or the ring size
   double inv_vpr;             // 1 / vectors per row
   float inv_vpr_f;
   int32_t lo[EP_NTABLES];
@@ -40,8 +41,10 @@ struct DecodeArgs {
 
 // Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).
 // `slow`: scale without the fused multiply-add (needed for bf16 when some row scale is tiny).
+// `ring`: stream each tile's words through an LDS ring of words_stride words (a power of two)
+// instead of holding the whole tile.
 template <int DT>
-hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, int waves,
-                         size_t lds, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool ring,
+                         int waves, size_t lds, hipStream_t s);
 
 }  // namespace ep

@@ -502,6 +502,14 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
 extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
                                    const void* d_dec_tables, void* d_out, uint32_t* d_err,
                                    void* stream) {
+  return ep_decompress_ex(d_blob, info, d_dec_tables, d_out, d_err, 0u, stream);
+}
+
+extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* info,
+                                      const void* d_dec_tables, void* d_out, uint32_t* d_err,
+                                      uint32_t flags, void* stream) {
+  const uint32_t layout = flags & (EP_DECODE_LINEAR | EP_DECODE_RING | EP_DECODE_RING_MIN);
+  if ((flags & ~layout) || (layout & (layout - 1u))) return EP_ERR_ARG;
   if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_blob) & 15u) || (reinterpret_cast<uintptr_t>(d_out) & 15u))
     return EP_ERR_ARG;
@@ -526,31 +534,53 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
   a.inv_vpr = 1.0 / (double)a.vpr;
   a.inv_vpr_f = 1.0f / (float)a.vpr;
   a.max_tile_words = info->max_tile_words;
-  // words region per wave: the aligned chunks of the largest tile plus one wave of slack
-  a.words_stride = ((info->max_tile_words + 7u + 7u) & ~7u) + 64u;
+  // Words region per wave.  Linear: the aligned chunks of the largest tile plus one wave of
+  // slack.  Ring: a power of two of at least 512 words and 2/7 of the largest tile (two field
+  // phases' worth), refilled as the tile is decoded; used only when it keeps more tiles resident.
+  const uint32_t lin_stride = ((info->max_tile_words + 7u + 7u) & ~7u) + 64u;
+  uint32_t ring_stride = 512u;
+  while (layout != EP_DECODE_RING_MIN && ring_stride < 8192u &&
+         (uint64_t)ring_stride * 7u < 2ull * info->max_tile_words)
+    ring_stride <<= 1;
   for (int t = 0; t < EP_NTABLES; t++) a.lo[t] = info->lo[t];
   a.coset_f0 = info->coset_freq0;
   // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
-  // per wave 256 B of states and the words region.  Waves per workgroup (8, 4, 2 or 1): the
-  // choice that keeps the most tiles resident at once, preferring more waves on ties.
+  // per wave 256 B of states and the words region.  Waves per workgroup and layout: the choice
+  // that keeps the most tiles resident at once; ties go to the linear layout, then to the smaller
+  // workgroup (spread over more CUs).
   const bool big = info->big_alphabet != 0;
   const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
-  auto lds_of = [&](int w) { return lds_tables + (size_t)w * (256 + (size_t)a.words_stride * 2); };
+  auto lds_of = [&](int w, uint32_t stride) {
+    return lds_tables + (size_t)w * (256 + (size_t)stride * 2);
+  };
   // waves per SIMD the decoder's registers allow: 8, 4 and 2 for 8, 16 and 32 vectors per lane
   const int64_t waves_per_cu = 4 * (J <= 8 ? 8 : (J <= 16 ? 4 : 2));
   const int max_waves = J <= 16 ? kDecWaves : kDecWaves / 2;
   int waves = 0;
+  bool ring = false;
   int64_t best = -1;
-  for (int w = max_waves; w >= 1; w >>= 1) {
-    if ((int64_t)lds_of(w) > kLdsPerCU) continue;
-    const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w), waves_per_cu / w);
-    const int64_t grid = (info->tiles + w - 1) / w;
-    const int64_t resident = std::min(grid, kCUs * per_cu) * w;
-    // most tiles in flight; on a tie, the smaller workgroup (spread over more CUs)
-    if (resident >= best) { best = resident; waves = w; }
+  for (int lay = 0; lay < 2; lay++) {
+    const bool rg = lay == 1;
+    if (layout == EP_DECODE_LINEAR && rg) continue;
+    if ((layout == EP_DECODE_RING || layout == EP_DECODE_RING_MIN) && !rg) continue;
+    if (rg && layout == 0 && ring_stride >= lin_stride) continue;
+    const uint32_t stride = rg ? ring_stride : lin_stride;
+    for (int w = max_waves; w >= 1; w >>= 1) {
+      if ((int64_t)lds_of(w, stride) > kLdsPerCU) continue;
+      const int64_t per_cu =
+          std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, stride), waves_per_cu / w);
+      const int64_t grid = (info->tiles + w - 1) / w;
+      const int64_t resident = std::min(grid, kCUs * per_cu) * w;
+      if (resident > best || (resident == best && !rg)) {
+        best = resident;
+        waves = w;
+        ring = rg;
+      }
+    }
   }
   if (waves == 0) return EP_ERR_VERSION;             // one tile's words do not fit in LDS
-  const size_t lds = lds_of(waves);
+  a.words_stride = ring ? ring_stride : lin_stride;
+  const size_t lds = lds_of(waves, a.words_stride);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t tiles = (uint32_t)info->tiles;
   const uint32_t V = (uint32_t)info->tile_fields / 8;
@@ -563,11 +593,12 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
     a.tile_begin = t0;
     a.tile_end = t1;
     switch (info->dtype) {
-      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, slow, waves, lds, s);
-      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, false, waves, lds, s);
+      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, slow, ring, waves, lds, s);
+      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, false, ring, waves, lds, s);
       case EP_FP8_E4M3FN:
-        return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, waves, lds, s);
-      default: return launch_decode<EP_INT8>(a, J, big, ragged, false, waves, lds, s);
+        return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, ring, waves,
+                                              lds, s);
+      default: return launch_decode<EP_INT8>(a, J, big, ragged, false, ring, waves, lds, s);
     }
   };
   if (full_tiles > 0 && launch(0, full_tiles, false) != hipSuccess) return EP_ERR_HIP;

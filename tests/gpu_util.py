@@ -101,15 +101,19 @@ class GpuBlob:
         esize = 2 if self.info.dtype in (1, 2) else 1
         return self.info.rows * self.info.cols * esize
 
-    def decode(self, d_out=None):
-        """Returns (err word, output container bits as numpy [rows, cols])."""
+    def decode(self, d_out=None, flags=None):
+        """Returns (err word, output container bits as numpy [rows, cols]).  flags: None for
+        ep_decompress, else the ep_decompress_ex layout flags."""
         import torch
 
         ep = ep_mod()
         if d_out is None:
             d_out = torch.zeros(self.out_bytes(), dtype=torch.uint8, device="cuda")
         d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
-        st = ep.ep_decompress(self.d_blob, self.info, self.d_tab, d_out, d_err)
+        if flags is None:
+            st = ep.ep_decompress(self.d_blob, self.info, self.d_tab, d_out, d_err)
+        else:
+            st = ep.ep_decompress_ex(self.d_blob, self.info, self.d_tab, d_out, d_err, flags)
         assert st == 0, st
         torch.cuda.synchronize()
         out = host(d_out)

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import ep_synth as S
-from gpu_util import GpuBlob, gpu_compress, gpu_quantize, gpu_row_lsq, gpu_row_sumsq, log
+from gpu_util import (GpuBlob, ep_mod, gpu_compress, gpu_quantize, gpu_row_lsq, gpu_row_sumsq,
+                      log)
 
 pytestmark = pytest.mark.gpu
 
@@ -184,6 +185,61 @@ def test_decode_detects_corrupt_tile(orc):
     assert err & (1 << 7)
     assert orc.decompress(bad)[0] == orc.ERR_CORRUPT
     assert info["tiles"] > 1
+
+
+LAYOUT_CASES = [
+    (2, 512, 1024, None),       # J = 16
+    (2, 200, 776, None),        # ragged
+    (3, 256, 1024, None),       # wide alphabet
+    ("5a", 64, 2048, None),     # J = 32
+    ("5b", 64, 2048, None),     # J = 32, wide alphabet, 6.6 bpp
+    ("5b", 37, 1000, None),     # ragged J = 32
+    (2, 128, 1024, 11.0),       # the highest rate: phases consume more than a small ring holds
+    (1, 256, 256, 8.0),         # J = 8
+]
+
+
+@pytest.mark.parametrize("flags", ["LINEAR", "RING", "RING_MIN"])
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-{c[3]}")
+def test_decode_word_layouts_match_oracle(orc, case, flags):
+    """Each tile's words held whole in LDS, or streamed through a ring (automatic size, and the
+    smallest ring, which refills in the middle of phases): the same bytes as the oracle."""
+    key, R, C, target = case
+    log("decode layout", case, flags)
+    ep = ep_mod()
+    w, blob = _oracle_blob(orc, key, R, C, target=target)
+    gb = GpuBlob(blob)
+    err, out = gb.decode(flags=getattr(ep, "EP_DECODE_" + flags))
+    st, ref, _, _ = orc.decompress(blob)
+    assert st == 0 and err == 0
+    assert np.array_equal(out, ref)
+
+
+def test_decode_ring_detects_corrupt_tile(orc):
+    log("decode ring corrupt")
+    ep = ep_mod()
+    w, blob = _oracle_blob(orc, 2, 256, 1024)
+    bad = blob.copy()
+    bad[-64] ^= 0x5A                                  # a payload word of the last tile
+    gb = GpuBlob(bad)
+    for flags in (ep.EP_DECODE_RING, ep.EP_DECODE_RING_MIN):
+        err, _ = gb.decode(flags=flags)
+        assert err & (1 << 7)
+
+
+def test_decode_layout_flags_rejected(orc):
+    import torch
+
+    ep = ep_mod()
+    w, blob = _oracle_blob(orc, 1, 256, 256)
+    gb = GpuBlob(blob)
+    d_out = torch.zeros(gb.out_bytes(), dtype=torch.uint8, device="cuda")
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for flags in (8, ep.EP_DECODE_LINEAR | ep.EP_DECODE_RING, 3 | 4):
+        assert ep.ep_decompress_ex(gb.d_blob, gb.info, gb.d_tab, d_out, d_err, flags) == \
+            ep.EP_ERR_ARG
+    torch.cuda.synchronize()
+    assert int(d_err.item()) == 0
 
 
 @pytest.mark.parametrize("case", [(1, 256, 256), (2, 256, 1024), (3, 128, 1024),
