@@ -21,8 +21,8 @@ constexpr int kDecWaves = 16;
 constexpr int64_t kCUs = 256;
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
-// Kernel arguments of the fused tile decoder.
-struct DecodeArgs {
+// One blob's part of the fused tile decoder's arguments.
+struct DecodeBlob {
   const float* alpha;         // f32[rows]
   const uint32_t* word_off;   // u32[tiles + 1]
   const uint32_t* states;     // u32[tiles][64]
@@ -30,13 +30,22 @@ struct DecodeArgs {
   const uint32_t* ent;        // slot entries f | (slot - cum) << 13 | value << 25: u32[16][4096]
   const int16_t* val;         // field value per slot: i16[16][4096]
   void* out;                  // container[rows][cols]
-  uint32_t* err;              // device error word
-  uint32_t tile_begin, tile_end;  // tiles decoded by this launch
+  uint32_t tile_begin, tile_end;  // tiles of this blob decoded by the launch
   uint32_t n_vec, vpr, max_tile_words, coset_f0;
-  uint32_t words_stride;       // words per wave region: the largest tile + slack, or the ring size
-  double inv_vpr;             // 1 / vectors per row
+  int32_t lo0;                // smallest coset value (table 0)
   float inv_vpr_f;
-  int32_t lo[EP_NTABLES];
+  double inv_vpr;             // 1 / vectors per row
+};
+
+// Kernel arguments of the fused tile decoder: up to kMaxBatch blobs per launch (same container,
+// tile size and LDS layout).  Workgroups [wg_begin[i], wg_begin[i + 1]) decode blob i.
+constexpr int kMaxBatch = 16;
+struct DecodeArgs {
+  uint32_t* err;              // device error word
+  uint32_t words_stride;      // words per wave region: the largest tile + slack, or the ring size
+  uint32_t n;
+  uint32_t wg_begin[kMaxBatch + 1];
+  DecodeBlob b[kMaxBatch];
 };
 
 // Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).

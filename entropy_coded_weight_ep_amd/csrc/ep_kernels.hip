@@ -499,56 +499,50 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
 }
 
 
-extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
-                                   const void* d_dec_tables, void* d_out, uint32_t* d_err,
-                                   void* stream) {
-  return ep_decompress_ex(d_blob, info, d_dec_tables, d_out, d_err, 0u, stream);
-}
-
-extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* info,
-                                      const void* d_dec_tables, void* d_out, uint32_t* d_err,
-                                      uint32_t flags, void* stream) {
+// Decodes n blobs of one container and tile size: the full tiles of all of them in launches of up
+// to kMaxBatch blobs, then the ragged last tiles (if any) the same way.
+static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_info* infos,
+                              const void* const* d_dec_tables, void* const* d_outs,
+                              uint32_t* d_err, uint32_t flags, hipStream_t s) {
   const uint32_t layout = flags & (EP_DECODE_LINEAR | EP_DECODE_RING | EP_DECODE_RING_MIN);
   if ((flags & ~layout) || (layout & (layout - 1u))) return EP_ERR_ARG;
-  if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(d_blob) & 15u) || (reinterpret_cast<uintptr_t>(d_out) & 15u))
-    return EP_ERR_ARG;
-  if (info->precision != EP_PRECISION || info->lanes != EP_LANES) return EP_ERR_VERSION;
-  if (info->dtype < EP_BF16 || info->dtype > EP_INT8) return EP_ERR_DTYPE;
-  const int J = info->tile_fields / (8 * EP_LANES);
-  if (info->tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
-  const int64_t nv = info->rows * info->cols / 8;
-  if (nv >= ((int64_t)1 << 31) || info->tiles < 1) return EP_ERR_SHAPE;
-  DecodeArgs a;
-  const uint8_t* b = static_cast<const uint8_t*>(d_blob);
-  a.alpha = reinterpret_cast<const float*>(b + info->off_alpha);
-  a.word_off = reinterpret_cast<const uint32_t*>(b + info->off_word_off);
-  a.states = reinterpret_cast<const uint32_t*>(b + info->off_states);
-  a.words = reinterpret_cast<const uint16_t*>(b + info->off_words);
-  a.ent = static_cast<const uint32_t*>(d_dec_tables);
-  a.val = reinterpret_cast<const int16_t*>(a.ent + 16 * kM);
-  a.out = d_out;
-  a.err = d_err;
-  a.n_vec = (uint32_t)nv;
-  a.vpr = (uint32_t)(info->cols / 8);
-  a.inv_vpr = 1.0 / (double)a.vpr;
-  a.inv_vpr_f = 1.0f / (float)a.vpr;
-  a.max_tile_words = info->max_tile_words;
+  if (n < 1 || !d_blobs || !infos || !d_dec_tables || !d_outs || !d_err) return EP_ERR_ARG;
+  const ep_blob_info& i0 = infos[0];
+  if (i0.dtype < EP_BF16 || i0.dtype > EP_INT8) return EP_ERR_DTYPE;
+  const int J = i0.tile_fields / (8 * EP_LANES);
+  if (i0.tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
+  // batch-wide choices: the largest tile, any wide alphabet, any tiny row scale
+  uint32_t maxw = 0;
+  bool big = false, slow = false;
+  int64_t total_tiles = 0;
+  for (int i = 0; i < n; i++) {
+    const ep_blob_info& in = infos[i];
+    if (!d_blobs[i] || !d_dec_tables[i] || !d_outs[i]) return EP_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_blobs[i]) & 15u) ||
+        (reinterpret_cast<uintptr_t>(d_outs[i]) & 15u))
+      return EP_ERR_ARG;
+    if (in.precision != EP_PRECISION || in.lanes != EP_LANES) return EP_ERR_VERSION;
+    if (in.dtype != i0.dtype || in.tile_fields != i0.tile_fields) return EP_ERR_ARG;
+    if (in.rows < 1 || in.cols < 8 || in.rows * in.cols / 8 >= ((int64_t)1 << 31) ||
+        in.tiles < 1 || in.tiles != (in.rows * in.cols / 8 + J * 64 - 1) / (J * 64))
+      return EP_ERR_SHAPE;
+    maxw = std::max(maxw, in.max_tile_words);
+    big |= in.big_alphabet != 0;
+    slow |= in.tiny_scale != 0;
+    total_tiles += in.tiles;
+  }
   // Words region per wave.  Linear: the aligned chunks of the largest tile plus one wave of
   // slack.  Ring: a power of two of at least 512 words and 2/7 of the largest tile (two field
   // phases' worth), refilled as the tile is decoded; used only when it keeps more tiles resident.
-  const uint32_t lin_stride = ((info->max_tile_words + 7u + 7u) & ~7u) + 64u;
+  const uint32_t lin_stride = ((maxw + 7u + 7u) & ~7u) + 64u;
   uint32_t ring_stride = 512u;
   while (layout != EP_DECODE_RING_MIN && ring_stride < 8192u &&
-         (uint64_t)ring_stride * 7u < 2ull * info->max_tile_words)
+         (uint64_t)ring_stride * 7u < 2ull * maxw)
     ring_stride <<= 1;
-  for (int t = 0; t < EP_NTABLES; t++) a.lo[t] = info->lo[t];
-  a.coset_f0 = info->coset_freq0;
   // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
   // per wave 256 B of states and the words region.  Waves per workgroup and layout: the choice
   // that keeps the most tiles resident at once; ties go to the linear layout, then to the smaller
   // workgroup (spread over more CUs).
-  const bool big = info->big_alphabet != 0;
   const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
   auto lds_of = [&](int w, uint32_t stride) {
     return lds_tables + (size_t)w * (256 + (size_t)stride * 2);
@@ -569,7 +563,7 @@ extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* in
       if ((int64_t)lds_of(w, stride) > kLdsPerCU) continue;
       const int64_t per_cu =
           std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, stride), waves_per_cu / w);
-      const int64_t grid = (info->tiles + w - 1) / w;
+      const int64_t grid = (total_tiles + w - 1) / w;
       const int64_t resident = std::min(grid, kCUs * per_cu) * w;
       if (resident > best || (resident == best && !rg)) {
         best = resident;
@@ -579,29 +573,90 @@ extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* in
     }
   }
   if (waves == 0) return EP_ERR_VERSION;             // one tile's words do not fit in LDS
-  a.words_stride = ring ? ring_stride : lin_stride;
-  const size_t lds = lds_of(waves, a.words_stride);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint32_t tiles = (uint32_t)info->tiles;
-  const uint32_t V = (uint32_t)info->tile_fields / 8;
-  const bool last_ragged = (uint64_t)tiles * V != (uint64_t)nv;
-  const uint32_t full_tiles = last_ragged ? tiles - 1 : tiles;
+  const uint32_t stride = ring ? ring_stride : lin_stride;
+  const size_t lds = lds_of(waves, stride);
+  const uint32_t V = (uint32_t)i0.tile_fields / 8;
+
+  DecodeArgs a;
+  a.err = d_err;
+  a.words_stride = stride;
+  auto flush = [&](bool ragged) -> ep_status {
+    if (a.n == 0) return EP_OK;
+    hipError_t e;
+    switch (i0.dtype) {
+      case EP_BF16: e = launch_decode<EP_BF16>(a, J, big, ragged, slow, ring, waves, lds, s); break;
+      case EP_FP16: e = launch_decode<EP_FP16>(a, J, big, ragged, false, ring, waves, lds, s); break;
+      case EP_FP8_E4M3FN:
+        e = launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, ring, waves, lds, s);
+        break;
+      default: e = launch_decode<EP_INT8>(a, J, big, ragged, false, ring, waves, lds, s); break;
+    }
+    a.n = 0;
+    return e == hipSuccess ? EP_OK : EP_ERR_HIP;
+  };
   // the fused scaling is exact for fp16, fp8 and int8 whatever the scales (a tiny scale's products
   // round to zero in those containers); bf16 keeps the subnormal range and needs the exact half
-  const bool slow = info->tiny_scale != 0;
-  auto launch = [&](uint32_t t0, uint32_t t1, bool ragged) -> hipError_t {
-    a.tile_begin = t0;
-    a.tile_end = t1;
-    switch (info->dtype) {
-      case EP_BF16: return launch_decode<EP_BF16>(a, J, big, ragged, slow, ring, waves, lds, s);
-      case EP_FP16: return launch_decode<EP_FP16>(a, J, big, ragged, false, ring, waves, lds, s);
-      case EP_FP8_E4M3FN:
-        return launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, ring, waves,
-                                              lds, s);
-      default: return launch_decode<EP_INT8>(a, J, big, ragged, false, ring, waves, lds, s);
+  for (int pass = 0; pass < 2; pass++) {             // full tiles, then ragged last tiles
+    const bool ragged = pass == 1;
+    a.n = 0;
+    a.wg_begin[0] = 0;
+    for (int i = 0; i < n; i++) {
+      const ep_blob_info& in = infos[i];
+      const int64_t nv = in.rows * in.cols / 8;
+      const uint32_t tiles = (uint32_t)in.tiles;
+      const bool last_ragged = (uint64_t)tiles * V != (uint64_t)nv;
+      const uint32_t t0 = ragged ? tiles - 1 : 0;
+      const uint32_t t1 = ragged ? tiles : (last_ragged ? tiles - 1 : tiles);
+      if ((ragged && !last_ragged) || t1 <= t0) continue;
+      DecodeBlob& b = a.b[a.n];
+      const uint8_t* p = static_cast<const uint8_t*>(d_blobs[i]);
+      b.alpha = reinterpret_cast<const float*>(p + in.off_alpha);
+      b.word_off = reinterpret_cast<const uint32_t*>(p + in.off_word_off);
+      b.states = reinterpret_cast<const uint32_t*>(p + in.off_states);
+      b.words = reinterpret_cast<const uint16_t*>(p + in.off_words);
+      b.ent = static_cast<const uint32_t*>(d_dec_tables[i]);
+      b.val = reinterpret_cast<const int16_t*>(b.ent + 16 * kM);
+      b.out = d_outs[i];
+      b.tile_begin = t0;
+      b.tile_end = t1;
+      b.n_vec = (uint32_t)nv;
+      b.vpr = (uint32_t)(in.cols / 8);
+      b.max_tile_words = in.max_tile_words;
+      b.coset_f0 = in.coset_freq0;
+      b.lo0 = in.lo[0];
+      b.inv_vpr_f = 1.0f / (float)b.vpr;
+      b.inv_vpr = 1.0 / (double)b.vpr;
+      a.wg_begin[a.n + 1] = a.wg_begin[a.n] + (t1 - t0 + waves - 1) / waves;
+      if (++a.n == kMaxBatch) {
+        const ep_status st = flush(ragged);
+        if (st != EP_OK) return st;
+        a.wg_begin[0] = 0;
+      }
     }
-  };
-  if (full_tiles > 0 && launch(0, full_tiles, false) != hipSuccess) return EP_ERR_HIP;
-  if (last_ragged && launch(tiles - 1, tiles, true) != hipSuccess) return EP_ERR_HIP;
+    const ep_status st = flush(ragged);
+    if (st != EP_OK) return st;
+  }
   return EP_OK;
+}
+
+extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
+                                   const void* d_dec_tables, void* d_out, uint32_t* d_err,
+                                   void* stream) {
+  return ep_decompress_ex(d_blob, info, d_dec_tables, d_out, d_err, 0u, stream);
+}
+
+extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* info,
+                                      const void* d_dec_tables, void* d_out, uint32_t* d_err,
+                                      uint32_t flags, void* stream) {
+  if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
+  return decode_blobs(1, &d_blob, info, &d_dec_tables, &d_out, d_err, flags,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" ep_status ep_decompress_batch(int32_t n, const void* const* d_blobs,
+                                         const ep_blob_info* infos,
+                                         const void* const* d_dec_tables, void* const* d_outs,
+                                         uint32_t* d_err, void* stream) {
+  return decode_blobs(n, d_blobs, infos, d_dec_tables, d_outs, d_err, 0u,
+                      static_cast<hipStream_t>(stream));
 }

@@ -227,6 +227,52 @@ def test_decode_ring_detects_corrupt_tile(orc):
         assert err & (1 << 7)
 
 
+def test_decode_batch_matches_oracle(orc):
+    """One batched decode of 20 blobs (two launches of up to 16; some ragged, some with wide
+    alphabets, different shapes) writes what 20 oracle decodes write."""
+    import torch
+
+    ep = ep_mod()
+    blobs, refs = [], []
+    shapes = [(64, 3072), (40, 1000), (96, 512), (8, 8), (128, 1024)]
+    for i in range(20):
+        R, C = shapes[i % len(shapes)]
+        key = 4 if i % 3 else 2
+        w = S.workload_weights(key, R, C, i)
+        target = 3.0 if i % 4 else 7.0                # 7 bpp: wide alphabets
+        st, blob, s = orc.compress(w, S.BF16, target, 8192)
+        assert st == 0
+        st, ref, _, _ = orc.decompress(blob)
+        assert st == 0
+        blobs.append(GpuBlob(blob))
+        refs.append(ref)
+    log("decode batch", len(blobs))
+    outs = [torch.zeros(b.out_bytes(), dtype=torch.uint8, device="cuda") for b in blobs]
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = ep.ep_decompress_batch([b.d_blob for b in blobs], [b.info for b in blobs],
+                                [b.d_tab for b in blobs], outs, d_err)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert int(d_err.item()) == 0
+    for b, o, ref in zip(blobs, outs, refs):
+        got = o.cpu().numpy().view(np.uint16).reshape(b.info.rows, b.info.cols)
+        assert np.array_equal(got, ref)
+
+
+def test_decode_batch_rejects_mixed_containers(orc):
+    import torch
+
+    ep = ep_mod()
+    a = GpuBlob(_oracle_blob(orc, 2, 64, 1024)[1])
+    w = S.workload_weights(3, 64, 1024)
+    st, blob, s = orc.compress(w, S.FP16, 3.0, 8192)
+    b = GpuBlob(blob)
+    outs = [torch.zeros(x.out_bytes(), dtype=torch.uint8, device="cuda") for x in (a, b)]
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert ep.ep_decompress_batch([a.d_blob, b.d_blob], [a.info, b.info], [a.d_tab, b.d_tab],
+                                  outs, d_err) == ep.EP_ERR_ARG
+
+
 def test_decode_layout_flags_rejected(orc):
     import torch
 
