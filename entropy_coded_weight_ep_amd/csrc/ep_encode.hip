@@ -1,0 +1,319 @@
+// GPU tile encoder (gfx950): the interleaved 64-state rANS encoding of the coset and field
+// symbols, tile by tile, producing the blob's tile offsets, final states and word stream.
+//
+// "The selected fields are encoded with rANS in independently decodable tiles" (EntroPack design
+// page, "Encoding and reconstruction"; rANS after Duda, "Asymmetric numeral systems", 2009; the
+// interleaving after Giesen, "Interleaved entropy coders", 2014).  The word order is the
+// decoder's: phases (coset, field 0..7), inside each the lane's vectors ascending, inside that the
+// lanes ascending.  The encoder walks that order backwards, so every tile's stream is the reverse
+// of the words in the order the encoder emits them.
+//
+// One wavefront encodes one tile, lane l owning state l and the vectors l, l+64, ..., l+64(J-1).
+// At each (phase, vector) step the lanes that must flush a word do so together; in the backward
+// order lane 63 comes first, so a flushing lane's word goes after those of the flushing lanes
+// above it.  The words go onto a per-tile stack in scratch memory in that order, with the tile's
+// count and its 64 final states (the decoder's initial states); a scan turns the counts into
+// offsets, and a copy writes every stack reversed into the blob's word stream.
+//
+// Per symbol: entry (f, cum) of value - lo in the table of this phase and coset; flush
+// x & 0xFFFF when x >= f * 2^20; then x = (x / f) * 2^12 + x mod f + cum.  x / f: the fp64
+// product of x and a reciprocal of f, truncated, then corrected exactly by one step either way
+// from the integer remainder.  The hardware fp64 reciprocal is only good to about 2^-23
+// relative; one Newton step squares that to about 2^-46, so for x < 2^32 the estimate is off by
+// less than 2^-13 and the one-step correction is exact.  The step has no branch: lanes without
+// a vector keep their state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+#include <vector>
+
+#include "ep.h"
+#include "ep_device.h"
+
+namespace ep {
+
+constexpr int kEncWaves = 4;                       // tiles (wavefronts) per workgroup
+constexpr uint32_t kEncLdsEntries = 16384;         // table entries held in LDS (64 KiB)
+
+// Where each table's entries start in the packed entry array, and its value range.
+struct EncTabs {
+  uint32_t off[EP_NTABLES];
+  uint32_t n[EP_NTABLES];
+  int32_t lo[EP_NTABLES];
+};
+
+// Field k (0..7) of a vector's packed fields (eight int16, two per word).
+__device__ __forceinline__ int32_t field_of(const uint4& q, int k) {
+  const uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
+  return (k & 1) ? (int32_t)w >> 16 : (int32_t)(int16_t)(w & 0xFFFFu);
+}
+
+template <int J, bool LDS_TAB>
+__global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
+    const uint8_t* __restrict__ coset, const int16_t* __restrict__ fields, uint32_t n_vec,
+    uint32_t tiles, const uint32_t* __restrict__ ent, uint32_t n_ent, EncTabs ta,
+    uint32_t* __restrict__ counts, uint32_t* __restrict__ states, uint16_t* __restrict__ stack,
+    uint32_t* __restrict__ err) {
+  extern __shared__ uint32_t s_ent[];
+  if constexpr (LDS_TAB) {
+    for (uint32_t i = threadIdx.x; i < n_ent; i += blockDim.x) s_ent[i] = ent[i];
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t t = blockIdx.x * kEncWaves + wave;
+  if (t >= tiles) return;
+  constexpr uint32_t V = 64u * J;
+  const uint32_t tv = t * V;
+  const uint32_t nvt = n_vec - tv < V ? n_vec - tv : V;
+
+  // the lane's vectors: packed fields and coset bits
+  uint4 fk[J];
+  uint32_t cbits = 0;
+  uint32_t bad = 0;                                 // a symbol outside its table
+#pragma unroll
+  for (int j = 0; j < J; j++) {
+    const uint32_t u = (uint32_t)lane + 64u * j;
+    fk[j] = make_uint4(0, 0, 0, 0);
+    if (u < nvt) {
+      fk[j] = reinterpret_cast<const uint4*>(fields)[tv + u];
+      const uint32_t cb = coset[tv + u];
+      bad |= cb > 1u ? 1u : 0u;
+      cbits |= (cb & 1u) << j;
+    }
+  }
+
+  uint32_t x = kL;
+  uint32_t sp = 0;                                  // words emitted so far (wave-uniform)
+  uint16_t* const stk = stack + (size_t)t * 9u * V; // room for one word per symbol
+#pragma unroll
+  for (int phase = 8; phase >= 0; --phase) {
+    // the two tables of this phase (coset 0 and coset 1; the coset phase has one), their
+    // parameters read here (the index is hidden from the compiler, which would otherwise keep
+    // all 17 tables' parameters in scalar registers across the whole unrolled loop)
+    int t0 = phase == 0 ? 0 : phase;
+    int t1 = phase == 0 ? 0 : 8 + phase;
+    asm volatile("" : "+s"(t0), "+s"(t1));
+    const int32_t lo0 = ta.lo[t0], lo1 = ta.lo[t1];
+    const uint32_t n0 = ta.n[t0], n1 = ta.n[t1];
+    const uint32_t off0 = ta.off[t0], off1 = ta.off[t1];
+#pragma unroll
+    for (int j = J - 1; j >= 0; --j) {
+      const bool valid = (uint32_t)lane + 64u * j < nvt;
+      const uint32_t c = (cbits >> j) & 1u;
+      int32_t value;
+      if (phase == 0) value = (int32_t)c;
+      else value = field_of(fk[j], phase - 1);
+      const uint32_t s = (uint32_t)(value - (c ? lo1 : lo0));
+      const uint32_t nt = c ? n1 : n0;
+      const bool in = s < nt;                       // (an empty table has nt = 0)
+      // an in-range index always (entry 0 of the packed array when the value is not in the table)
+      const uint32_t idx = in ? (c ? off1 : off0) + s : 0u;
+      uint32_t e;
+      if constexpr (LDS_TAB) e = s_ent[idx];
+      else e = ent[idx];
+      const bool ok = !valid || (in && (e & 0x1FFFu) != 0u);
+      bad |= ok ? 0u : 1u;
+      const bool use = valid && ok;
+      const uint32_t f = use ? (e & 0x1FFFu) : 1u;
+      const uint32_t cum = e >> 13;
+      const bool flush = use && (uint64_t)x >= ((uint64_t)f << (32 - EP_PRECISION));
+      const uint64_t m = __ballot(flush);
+      if (flush) {
+        // emission index: the flushing lanes above this one come first
+        const uint32_t above =
+            (uint32_t)__popcll(m) -
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) -
+            1u;
+        stk[sp + above] = (uint16_t)(x & 0xFFFFu);
+      }
+      sp += (uint32_t)__popcll(m);
+      {
+        const uint32_t xs = flush ? x >> 16 : x;
+        const double fd = (double)f;
+        double rc = __builtin_amdgcn_rcp(fd);
+        rc = __builtin_fma(__builtin_fma(-fd, rc, 1.0), rc, rc);
+        uint32_t q = (uint32_t)((double)xs * rc);
+        int32_t r = (int32_t)(xs - q * f);
+        q = r < 0 ? q - 1u : (r >= (int32_t)f ? q + 1u : q);
+        r = r < 0 ? r + (int32_t)f : (r >= (int32_t)f ? r - (int32_t)f : r);
+        const uint32_t xn = (q << EP_PRECISION) + (uint32_t)r + cum;
+        x = use ? xn : x;
+      }
+    }
+  }
+  if (__ballot(bad != 0u) != 0ull && lane == 0) atomicOr(err, 1u << EP_ERR_ALPHABET);
+  states[(size_t)t * 64 + lane] = x;
+  if (lane == 0) counts[t] = sp;
+}
+
+// Exclusive scan of the tile word counts -> word_off[0..tiles] and the largest count; one
+// workgroup, 1024 tiles per round.
+__global__ __launch_bounds__(1024) void k_scan_offsets(const uint32_t* __restrict__ counts,
+                                                       uint32_t tiles,
+                                                       uint32_t* __restrict__ word_off,
+                                                       uint32_t* __restrict__ max_count,
+                                                       uint64_t words_cap,
+                                                       uint32_t* __restrict__ err) {
+  __shared__ uint32_t s[1024];
+  __shared__ uint32_t s_max[1024];
+  uint64_t carry = 0;
+  uint32_t mx = 0;
+  for (uint32_t b = 0; b < tiles; b += 1024) {
+    const uint32_t i = b + threadIdx.x;
+    const uint32_t v = i < tiles ? counts[i] : 0u;
+    s[threadIdx.x] = v;
+    mx = v > mx ? v : mx;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024; d <<= 1) {      // inclusive Hillis-Steele scan
+      const uint32_t add = threadIdx.x >= d ? s[threadIdx.x - d] : 0u;
+      __syncthreads();
+      s[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const uint64_t incl = carry + s[threadIdx.x];
+    if (i < tiles) {
+      if (incl > 0xFFFFFFFFull) atomicOr(err, 1u << EP_ERR_CAPACITY);
+      word_off[i + 1] = (uint32_t)incl;
+    }
+    carry += s[1023];
+    __syncthreads();
+  }
+  s_max[threadIdx.x] = mx;
+  __syncthreads();
+  for (uint32_t d = 512; d > 0; d >>= 1) {
+    if (threadIdx.x < d && s_max[threadIdx.x + d] > s_max[threadIdx.x])
+      s_max[threadIdx.x] = s_max[threadIdx.x + d];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    word_off[0] = 0;
+    *max_count = s_max[0];
+    if (carry > words_cap) atomicOr(err, 1u << EP_ERR_CAPACITY);
+  }
+}
+
+// Each tile's stack, reversed, into the word stream at word_off[t] (one workgroup per tile).
+__global__ __launch_bounds__(256) void k_copy_words(const uint16_t* __restrict__ stack,
+                                                    uint32_t stack_words,
+                                                    const uint32_t* __restrict__ word_off,
+                                                    uint16_t* __restrict__ words,
+                                                    uint64_t words_cap) {
+  const uint32_t t = blockIdx.x;
+  const uint32_t b = word_off[t], cnt = word_off[t + 1] - b;
+  if (cnt > stack_words) return;                   // (never: a tile has at most one word a symbol)
+  const uint16_t* stk = stack + (size_t)t * stack_words;
+  for (uint32_t i = threadIdx.x; i < cnt; i += 256) {
+    if ((uint64_t)b + i < words_cap) words[(uint64_t)b + i] = stk[cnt - 1u - i];
+  }
+}
+
+template <int J, bool LDS_TAB>
+static void launch_enc(dim3 grid, size_t lds, hipStream_t s, const uint8_t* coset,
+                       const int16_t* fields, uint32_t nv, uint32_t tiles, const uint32_t* ent,
+                       uint32_t n_ent, const EncTabs& ta, uint32_t* counts, uint32_t* states,
+                       uint16_t* stack, uint32_t* err) {
+  k_encode_tiles<J, LDS_TAB><<<grid, 64 * kEncWaves, lds, s>>>(coset, fields, nv, tiles, ent,
+                                                               n_ent, ta, counts, states, stack,
+                                                               err);
+}
+
+// Workspace layout: packed table entries, tile counts, per-tile word stacks (9V words each).
+struct EncWs {
+  uint32_t* ent;
+  uint32_t* counts;
+  uint16_t* stack;
+  size_t total;
+};
+
+static EncWs enc_carve(void* base, int64_t n_vectors, uint32_t tile_fields) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const int64_t V = tile_fields / 8;
+  const int64_t tiles = (n_vectors + V - 1) / V;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t o = 0;
+  EncWs w;
+  w.ent = reinterpret_cast<uint32_t*>(p + o); o += up((size_t)4 * EP_NTABLES * EP_HIST_BINS);
+  w.counts = reinterpret_cast<uint32_t*>(p + o); o += up((size_t)4 * tiles);
+  w.stack = reinterpret_cast<uint16_t*>(p + o); o += up((size_t)2 * 9 * V * tiles);
+  w.total = o;
+  return w;
+}
+
+}  // namespace ep
+
+using namespace ep;
+
+extern "C" size_t ep_encode_workspace_bytes(int64_t n_vectors, uint32_t tile_fields) {
+  if (n_vectors < 1 || tile_fields < 512 || tile_fields % 512) return 0;
+  return enc_carve(nullptr, n_vectors, tile_fields).total;
+}
+
+extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* d_fields,
+                                         int64_t n_vectors, uint32_t tile_fields,
+                                         const ep_tables* h_tables, void* d_workspace,
+                                         size_t workspace_bytes, uint32_t* d_word_off,
+                                         uint32_t* d_max_tile_words, uint32_t* d_states,
+                                         uint16_t* d_words, int64_t words_cap, uint32_t* d_err,
+                                         void* stream) {
+  if (!d_coset || !d_fields || !h_tables || !d_workspace || !d_word_off || !d_max_tile_words ||
+      !d_states || !d_words || !d_err || words_cap < 0)
+    return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
+  if (n_vectors < 1 || n_vectors >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
+  const int J = (int)(tile_fields / (8 * EP_LANES));
+  if (tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_ARG;
+  if (workspace_bytes < ep_encode_workspace_bytes(n_vectors, tile_fields)) return EP_ERR_CAPACITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t nv = (uint32_t)n_vectors;
+  const uint32_t V = tile_fields / 8;
+  const uint32_t tiles = (uint32_t)((n_vectors + V - 1) / V);
+  const EncWs ws = enc_carve(d_workspace, n_vectors, tile_fields);
+
+  // packed entries f | cum << 13 of every table, in table order
+  EncTabs ta;
+  std::vector<uint32_t> ent;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    ta.off[t] = (uint32_t)ent.size();
+    ta.n[t] = h_tables->n[t];
+    ta.lo[t] = h_tables->lo[t];
+    if (ta.n[t] > EP_HIST_BINS) return EP_ERR_ARG;
+    uint32_t cum = 0;
+    for (uint32_t i = 0; i < ta.n[t]; i++) {
+      const uint32_t f = h_tables->freq[(size_t)t * EP_HIST_BINS + i];
+      ent.push_back(f | (cum << 13));
+      cum += f;
+    }
+    if (ta.n[t] && cum != (1u << EP_PRECISION)) return EP_ERR_ARG;
+  }
+  if (ent.empty()) ent.push_back(0);
+  const uint32_t n_ent = (uint32_t)ent.size();
+  if (hipMemcpyAsync(ws.ent, ent.data(), 4 * (size_t)n_ent, hipMemcpyHostToDevice, s) !=
+      hipSuccess)
+    return EP_ERR_HIP;
+  const dim3 grid((tiles + kEncWaves - 1) / kEncWaves);
+  const bool lds_tab = n_ent <= kEncLdsEntries;
+  const size_t lds = lds_tab ? 4 * (size_t)n_ent : 0;
+  auto go = [&](auto jc, auto lc) {
+    launch_enc<decltype(jc)::value, decltype(lc)::value>(grid, lds, s, d_coset, d_fields, nv,
+                                                          tiles, ws.ent, n_ent, ta, ws.counts,
+                                                          d_states, ws.stack, d_err);
+  };
+  using T8 = std::integral_constant<int, 8>;
+  using T16 = std::integral_constant<int, 16>;
+  using T32 = std::integral_constant<int, 32>;
+  auto by_j = [&](auto lc) {
+    if (J == 8) go(T8{}, lc);
+    else if (J == 16) go(T16{}, lc);
+    else go(T32{}, lc);
+  };
+  if (lds_tab) by_j(std::true_type{});
+  else by_j(std::false_type{});
+  k_scan_offsets<<<1, 1024, 0, s>>>(ws.counts, tiles, d_word_off, d_max_tile_words,
+                                    (uint64_t)words_cap, d_err);
+  k_copy_words<<<tiles, 256, 0, s>>>(ws.stack, 9 * V, d_word_off, d_words, (uint64_t)words_cap);
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}

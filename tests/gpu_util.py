@@ -134,3 +134,35 @@ def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
                                force_scale=force_scale)
     c = ep.compress(t, cfg)
     return c.blob, c.scale
+
+
+def gpu_encode_tiles(cos: np.ndarray, fld: np.ndarray, tile_fields: int, tables: np.ndarray,
+                     words_cap=None, d_fields_offset_bytes: int = 0):
+    """ep_encode_tiles_gpu on device copies of the symbols -> (status, err word, word_off,
+    max_tile_words, states, words[:min(word_off[-1], cap)]).  tables: ep_tables byte layout."""
+    import torch
+
+    ep = ep_mod()
+    nv = int(cos.size)
+    V = tile_fields // 8
+    T = (nv + V - 1) // V
+    cap = 9 * nv + 1 if words_cap is None else int(words_cap)
+    d_cos = dev(np.ascontiguousarray(cos, np.uint8))
+    raw = np.zeros(nv * 16 + 64, np.uint8)
+    d_raw = dev(raw)
+    d_fld = d_raw[d_fields_offset_bytes:d_fields_offset_bytes + nv * 16]
+    d_fld.copy_(dev(np.ascontiguousarray(fld, np.int16).view(np.uint8)))
+    wsb = ep.ep_encode_workspace_bytes(nv, tile_fields)
+    d_ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    d_woff = torch.full((T + 1,), -1, dtype=torch.int32, device="cuda")
+    d_max = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_states = torch.zeros(max(T, 1) * 64, dtype=torch.int32, device="cuda")
+    d_words = torch.zeros(max(cap, 1), dtype=torch.int16, device="cuda")
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = ep.ep_encode_tiles_gpu(d_cos, d_fld, nv, tile_fields, tables, d_ws, wsb, d_woff, d_max,
+                                d_states, d_words, cap, d_err)
+    torch.cuda.synchronize()
+    woff = host(d_woff).view(np.uint32)
+    n = min(int(woff[-1]), cap) if st == 0 else 0
+    return (st, int(host(d_err)[0]), woff, int(host(d_max).view(np.uint32)[0]),
+            host(d_states).view(np.uint32), host(d_words).view(np.uint16)[:n])

@@ -173,3 +173,15 @@ def test_compress_bound_covers_blobs(ep, orc):
         assert blob.size <= ep.ep_compress_bound(R, Cc, wl["tile_fields"])
     with pytest.raises(ep.EPError):
         ep.ep_compress_bound(4, 12, 4096)
+
+
+def test_encode_workspace_bytes(ep):
+    # tables (17 x 65536 u32) + counts + one 9V-word stack per tile, each part 256-byte aligned
+    up = lambda b: (b + 255) // 256 * 256
+    for nv, F in [(1, 4096), (4773, 4096), (32768, 8192), (18441, 16384)]:
+        V = F // 8
+        T = (nv + V - 1) // V
+        want = up(4 * 17 * 65536) + up(4 * T) + up(2 * 9 * V * T)
+        assert ep.ep_encode_workspace_bytes(nv, F) == want
+    assert ep.ep_encode_workspace_bytes(0, 4096) == 0
+    assert ep.ep_encode_workspace_bytes(100, 1000) == 0
