@@ -208,9 +208,22 @@ extern "C" ep_status ep_build_tables(const ep_hist* h_hist, uint32_t precision_b
   return EP_OK;
 }
 
+namespace {
+// Bits per element from the sampled symbols' coded size `acc` (bits) and the table sizes:
+// the sample scaled to all rows, plus every byte of the blob before the payload words.
+double finish_estimate(double acc, const uint32_t* n, int64_t rows, int64_t cols,
+                       int64_t n_sample_rows, uint32_t tile_fields) {
+  const double bits = acc * ((double)rows / (double)n_sample_rows);
+  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
+  const Layout L = layout(rows, tiles, tables_bytes(n), 0);
+  const double meta = (double)L.words;      // everything before the payload words
+  return (bits + 8.0 * meta) / ((double)rows * (double)cols);
+}
+}  // namespace
+
 extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t cols,
                                   int64_t n_sample_rows, uint32_t tile_fields) {
-  if (!h_hist || rows < 1 || cols < 8 || n_sample_rows < 1) return INFINITY;
+  if (!h_hist || rows < 1 || cols < 8 || n_sample_rows < 1 || tile_fields < 8) return INFINITY;
   std::vector<ep_tables> tv(1);
   ep_tables& T = tv[0];
   if (ep_build_tables(h_hist, EP_PRECISION, &T) != EP_OK) return INFINITY;
@@ -223,11 +236,23 @@ extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t c
       acc = acc + (double)c[i] * ((double)EP_PRECISION - std::log2(f));
     }
   }
-  const double bits = acc * ((double)rows / (double)n_sample_rows);
-  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
-  const Layout L = layout(rows, tiles, tables_bytes(T.n), 0);
-  const double meta = (double)L.words;      // everything before the payload words
-  return (bits + 8.0 * meta) / ((double)rows * (double)cols);
+  return finish_estimate(acc, T.n, rows, cols, n_sample_rows, tile_fields);
+}
+
+extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64_t cols,
+                                      int64_t n_sample_rows, uint32_t tile_fields,
+                                      void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!d_hist || !d_workspace || rows < 1 || cols < 8 || n_sample_rows < 1 || tile_fields < 8)
+    return INFINITY;
+  if (workspace_bytes < ep_estimate_workspace_bytes()) return INFINITY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double bits = 0.0;
+  uint32_t err = 0, n[EP_NTABLES];
+  if (!ep::estimate_enqueue(d_hist, d_workspace, true, s, &bits, &err, n) ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return NAN;
+  if (err) return INFINITY;
+  return finish_estimate(bits, n, rows, cols, n_sample_rows, tile_fields);
 }
 
 extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fields,
@@ -302,8 +327,18 @@ struct Workspace {
   uint32_t* err;
   uint8_t* coset;
   int16_t* fields;
+  void* rate;           // device rate estimate (tables, cost table, sums)
+  void* enc;            // device tile encoder workspace
+  size_t enc_bytes;
+  uint32_t* word_off;   // encoder outputs: u32[tiles + 1], u32[1], u32[tiles * 64], u16[9 NV + 1]
+  uint32_t* max_words;
+  uint32_t* states;
+  uint16_t* words;
   size_t total;
 };
+
+// Tile sizes the device tile encoder (and the device decoder) handle: 8, 16 or 32 vectors a lane.
+inline bool device_tile_size(uint32_t F) { return F == 4096 || F == 8192 || F == 16384; }
 
 Workspace carve(void* base, int64_t rows, int64_t cols) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
@@ -320,6 +355,17 @@ Workspace carve(void* base, int64_t rows, int64_t cols) {
   w.err = reinterpret_cast<uint32_t*>(p + o); o += up(4);
   w.coset = p + o; o += up(nv);
   w.fields = reinterpret_cast<int16_t*>(p + o); o += up(2 * 8 * nv);
+  w.rate = p + o; o += up(ep_estimate_workspace_bytes());
+  // the device encoder's workspace and outputs, sized for the smallest tiles it takes (the
+  // most tiles) and the largest (the most rounding of the last tile)
+  w.enc_bytes = std::max({ep_encode_workspace_bytes(nv, 4096), ep_encode_workspace_bytes(nv, 8192),
+                          ep_encode_workspace_bytes(nv, 16384)});
+  const int64_t max_tiles = (nv + 511) / 512;
+  w.enc = p + o; o += up(w.enc_bytes);
+  w.word_off = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (max_tiles + 1));
+  w.max_words = reinterpret_cast<uint32_t*>(p + o); o += up(4);
+  w.states = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)kK * max_tiles);
+  w.words = reinterpret_cast<uint16_t*>(p + o); o += up(2 * (9 * (size_t)nv + 1));
   w.total = o;
   return w;
 }
@@ -462,33 +508,26 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   for (double v : sumsq)
     if (!std::isfinite(v)) return EP_ERR_NONFINITE;
 
-  std::vector<ep_hist> hist_host(1);
   std::vector<float> gains(rows, 0.0f);
   uint32_t err_host = 0;
+  const uint32_t zero = 0;
 
-  // quantise (a subset of) rows at scale sc and fetch the histogram; returns the error bits
-  auto quantise = [&](double sc, const int64_t* d_sel, int64_t nsel, const std::vector<int64_t>& sel)
-      -> uint32_t {
+  // enqueue the quantisation of (a subset of) rows at scale sc, with its histogram
+  auto quantise = [&](double sc, const int64_t* d_sel, int64_t nsel,
+                      const std::vector<int64_t>& sel) -> ep_status {
     if (d_sel) {
       for (int64_t r : sel) gains[r] = row_gain(sumsq[r], cols, sc);
     } else {
       for (int64_t r = 0; r < rows; r++) gains[r] = row_gain(sumsq[r], cols, sc);
     }
-    uint32_t zero = 0;
     hip(hipMemcpyAsync(ws.gains, gains.data(), 4 * rows, hipMemcpyHostToDevice, s));
     hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
-    const ep_status q = ep_quantize_e8(d_w, dtype, rows, cols, ws.gains, d_sel, nsel, ws.coset,
-                                       ws.fields, ws.hist, ws.err, stream);
-    if (q != EP_OK) return 1u << q;
-    hip(hipMemcpyAsync(hist_host[0].counts, ws.hist->counts, sizeof(ep_hist),
-                       hipMemcpyDeviceToHost, s));
-    hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
-    hip(hipStreamSynchronize(s));
-    if (!hip.ok()) return 1u << EP_ERR_HIP;
-    return err_host;
+    return ep_quantize_e8(d_w, dtype, rows, cols, ws.gains, d_sel, nsel, ws.coset, ws.fields,
+                          ws.hist, ws.err, stream);
   };
 
-  // 2. rate search on sampled rows
+  // 2. rate search on sampled rows: per candidate the device quantises the sample, builds the
+  // tables and sums the coded bits; the host gets the sum and the table sizes
   double sc;
   if (forced) {
     sc = cfg->force_scale;
@@ -498,11 +537,19 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     std::vector<int64_t> sel(ns);
     for (int64_t i = 0; i < ns; i++) sel[i] = (i * rows) / ns;
     hip(hipMemcpyAsync(ws.rows_sel, sel.data(), 8 * ns, hipMemcpyHostToDevice, s));
+    bool cost_sent = false;
     auto est = [&](double scale) -> double {
-      const uint32_t e = quantise(scale, ws.rows_sel, ns, sel);
-      if (e & (1u << EP_ERR_HIP)) return NAN;
-      if (e) return INFINITY;
-      return ep_estimate_bpp(hist_host.data(), rows, cols, ns, F);
+      const ep_status q = quantise(scale, ws.rows_sel, ns, sel);
+      if (q != EP_OK) return q == EP_ERR_HIP ? NAN : INFINITY;
+      double bits = 0.0;
+      uint32_t terr = 0, n[EP_NTABLES];
+      if (!ep::estimate_enqueue(ws.hist, ws.rate, !cost_sent, s, &bits, &terr, n)) return NAN;
+      cost_sent = true;
+      hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+      hip(hipStreamSynchronize(s));
+      if (!hip.ok()) return NAN;
+      if (err_host || terr) return INFINITY;
+      return finish_estimate(bits, n, rows, cols, ns, F);
     };
     double lo = -20.0, hi = 12.0;
     const double target = cfg->target_bpp;
@@ -529,52 +576,82 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   }
   if (scale_out) *scale_out = sc;
 
-  // 3. full quantisation + histogram
-  {
-    const std::vector<int64_t> none;
-    const uint32_t e = quantise(sc, nullptr, rows, none);
-    if (e & (1u << EP_ERR_HIP)) return EP_ERR_HIP;
-    if (e & (1u << EP_ERR_RANGE)) return EP_ERR_RANGE;
-    if (e) return EP_ERR_ARG;
-  }
-  // 4. row least-squares scales
+  // 3. full quantisation + histogram, 4. row least-squares scales, 5. tables (device)
   std::vector<double> num(rows);
   std::vector<int64_t> den4(rows);
-  if ((st = ep_row_lsq(d_w, dtype, rows, cols, ws.coset, ws.fields, ws.num, ws.den4, stream)) != EP_OK)
-    return st;
-  std::vector<uint8_t> coset(nv);
-  std::vector<int16_t> fields(8 * nv);
-  hip(hipMemcpyAsync(num.data(), ws.num, 8 * rows, hipMemcpyDeviceToHost, s));
-  hip(hipMemcpyAsync(den4.data(), ws.den4, 8 * rows, hipMemcpyDeviceToHost, s));
-  hip(hipMemcpyAsync(coset.data(), ws.coset, nv, hipMemcpyDeviceToHost, s));
-  hip(hipMemcpyAsync(fields.data(), ws.fields, 16 * nv, hipMemcpyDeviceToHost, s));
-  hip(hipStreamSynchronize(s));
-  if (!hip.ok()) return EP_ERR_HIP;
+  std::vector<ep_tables> tabv(1);
+  ep_tables& T = tabv[0];
+  {
+    const std::vector<int64_t> none;
+    const ep_status q = quantise(sc, nullptr, rows, none);
+    if (q != EP_OK) return q == EP_ERR_HIP ? EP_ERR_HIP : EP_ERR_ARG;
+    if ((st = ep_row_lsq(d_w, dtype, rows, cols, ws.coset, ws.fields, ws.num, ws.den4, stream)) !=
+        EP_OK)
+      return st;
+    ep_tables* d_T = const_cast<ep_tables*>(ep::estimate_tables(ws.rate));
+    if ((st = ep_build_tables_gpu(ws.hist, d_T, ws.err, stream)) != EP_OK) return st;
+    hip(hipMemcpyAsync(num.data(), ws.num, 8 * rows, hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(den4.data(), ws.den4, 8 * rows, hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(&T, d_T, sizeof(ep_tables), hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+    hip(hipStreamSynchronize(s));
+    if (!hip.ok()) return EP_ERR_HIP;
+    if (err_host & (1u << EP_ERR_RANGE)) return EP_ERR_RANGE;
+    if (err_host & ~(1u << EP_ERR_ALPHABET)) return EP_ERR_ARG;
+    if (err_host) return EP_ERR_ALPHABET;
+  }
   std::vector<float> alpha(rows);
   for (int64_t r = 0; r < rows; r++)
     alpha[r] = den4[r] == 0 ? 0.0f : (float)(num[r] / ((double)den4[r] / 4.0));
 
-  // 5. tables
-  std::vector<ep_tables> tabv(1);
-  ep_tables& T = tabv[0];
-  if ((st = ep_build_tables(hist_host.data(), EP_PRECISION, &T)) != EP_OK) return st;
-
-  // 6. tiles
+  // 6. tiles (device encoder for the tile sizes it takes, else the host encoder), 7. blob
   const int64_t V = F / 8, tiles = (nv + V - 1) / V;
-  std::vector<uint32_t> word_off(tiles + 1), states(tiles * kK);
-  std::vector<uint16_t> words(9 * nv + 1);
-  if ((st = ep_encode_tiles(coset.data(), fields.data(), nv, F, &T, word_off.data(),
-                            states.data(), words.data(), (int64_t)words.size())) != EP_OK)
-    return st;
-  const int64_t W = word_off[tiles];
-
-  // 7. blob
   const int64_t tb = tables_bytes(T.n);
-  const Layout L = layout(rows, tiles, tb, W);
-  *out_bytes = (size_t)L.total;
-  if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
+  std::vector<uint32_t> word_off(tiles + 1);
   uint8_t* b = static_cast<uint8_t*>(h_blob);
-  std::memset(b, 0, (size_t)L.total);
+  Layout L;
+  int64_t W;
+  if (device_tile_size(F)) {
+    hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
+    if ((st = ep_encode_tiles_gpu(ws.coset, ws.fields, nv, F, &T, ws.enc, ws.enc_bytes,
+                                  ws.word_off, ws.max_words, ws.states, ws.words,
+                                  9 * nv + 1, ws.err, stream)) != EP_OK)
+      return st;
+    hip(hipMemcpyAsync(word_off.data(), ws.word_off, 4 * (tiles + 1), hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+    hip(hipStreamSynchronize(s));
+    if (!hip.ok()) return EP_ERR_HIP;
+    if (err_host) return EP_ERR_ARG;
+    W = word_off[tiles];
+    L = layout(rows, tiles, tb, W);
+    *out_bytes = (size_t)L.total;
+    if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
+    std::memset(b, 0, (size_t)L.total);
+    hip(hipMemcpyAsync(b + L.states, ws.states, 4 * kK * tiles, hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(b + L.words, ws.words, 2 * W, hipMemcpyDeviceToHost, s));
+    hip(hipStreamSynchronize(s));
+    if (!hip.ok()) return EP_ERR_HIP;
+  } else {
+    std::vector<uint8_t> coset(nv);
+    std::vector<int16_t> fields(8 * nv);
+    hip(hipMemcpyAsync(coset.data(), ws.coset, nv, hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(fields.data(), ws.fields, 16 * nv, hipMemcpyDeviceToHost, s));
+    hip(hipStreamSynchronize(s));
+    if (!hip.ok()) return EP_ERR_HIP;
+    std::vector<uint32_t> states(tiles * kK);
+    std::vector<uint16_t> words(9 * nv + 1);
+    if ((st = ep_encode_tiles(coset.data(), fields.data(), nv, F, &T, word_off.data(),
+                              states.data(), words.data(), (int64_t)words.size())) != EP_OK)
+      return st;
+    W = word_off[tiles];
+    L = layout(rows, tiles, tb, W);
+    *out_bytes = (size_t)L.total;
+    if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
+    std::memset(b, 0, (size_t)L.total);
+    std::memcpy(b + L.states, states.data(), 4 * kK * tiles);
+    std::memcpy(b + L.words, words.data(), 2 * W);
+  }
+
   std::memcpy(b, "EPK1", 4);
   const uint16_t version = 1;
   std::memcpy(b + 4, &version, 2);
@@ -602,7 +679,5 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   }
   std::memcpy(b + L.alpha, alpha.data(), 4 * rows);
   std::memcpy(b + L.word_off, word_off.data(), 4 * (tiles + 1));
-  std::memcpy(b + L.states, states.data(), 4 * kK * tiles);
-  std::memcpy(b + L.words, words.data(), 2 * W);
   return EP_OK;
 }

@@ -56,4 +56,13 @@ template <int DT>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool ring,
                          int waves, size_t lds, hipStream_t s);
 
+// Device part of the rate estimate (ep_rate.hip): enqueue on `s` the table build of d_hist and
+// the coded-bit sum of its symbols into the rate workspace (the cost table is copied in when
+// upload_cost), then copies of the sum, the error word and the 17 table sizes to the host
+// pointers, which are valid once `s` has synchronised.  False on a HIP error.
+bool estimate_enqueue(const ep_hist* d_hist, void* d_workspace, bool upload_cost, hipStream_t s,
+                      double* h_bits, uint32_t* h_err, uint32_t* h_n);
+// The device tables inside a rate workspace.
+const ep_tables* estimate_tables(void* d_workspace);
+
 }  // namespace ep

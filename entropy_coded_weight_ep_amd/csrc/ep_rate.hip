@@ -1,0 +1,250 @@
+// Device side of the rate search (gfx950): the table normalisation of a device histogram and
+// the coded-size sum of the sampled symbols, so that a scale candidate costs the host a few
+// hundred bytes of transfer instead of the whole 17 x 65536 histogram.
+//
+// The design page ("Rate selection and refinement") picks the scale from sampled rows by
+// estimating the coded field size plus the metadata for each candidate, without encoding the
+// full stream.  Here the estimate's two data-heavy parts run on the device:
+//   k_build_tables  one workgroup per table: the table's span [first, last] of seen values, then
+//                   the same integer normalisation as the host table build (frequency 0 for an
+//                   unseen value, else max(1, floor(count * 2^P / total)); a deficit goes to the
+//                   most frequent value, an excess is taken from the largest frequencies, lowest
+//                   index first on ties);
+//   k_sum_bits      one wavefront: the sum over tables, then values, of count * (P - log2 f) in
+//                   exactly the host's order, with every product and sum rounded on its own, so
+//                   the result is the host's double bit for bit (P - log2 f comes from a table
+//                   the host fills with its own log2).
+// The host finishes the estimate (sampling factor and metadata bytes) from that sum and the
+// tables' sizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <array>
+#include <cmath>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+constexpr uint32_t kNormM = 1u << EP_PRECISION;
+constexpr int kBT = 1024;                          // threads of a table-build workgroup
+
+// Largest 64-bit key of a workgroup (every thread passes one; all threads get the result).
+__device__ uint64_t block_max_u64(uint64_t v, uint64_t* s) {
+  s[threadIdx.x] = v;
+  __syncthreads();
+  for (int d = kBT / 2; d > 0; d >>= 1) {
+    if ((int)threadIdx.x < d && s[threadIdx.x + d] > s[threadIdx.x]) s[threadIdx.x] = s[threadIdx.x + d];
+    __syncthreads();
+  }
+  const uint64_t r = s[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* s) {
+  s[threadIdx.x] = v;
+  __syncthreads();
+  for (int d = kBT / 2; d > 0; d >>= 1) {
+    if ((int)threadIdx.x < d) s[threadIdx.x] += s[threadIdx.x + d];
+    __syncthreads();
+  }
+  const uint64_t r = s[0];
+  __syncthreads();
+  return r;
+}
+
+// Table t = blockIdx.x of the histogram -> lo[t], n[t], freq[t][0..n) of the device ep_tables.
+__global__ __launch_bounds__(kBT) void k_build_tables(const uint32_t* __restrict__ hist,
+                                                     ep_tables* __restrict__ out,
+                                                     uint32_t* __restrict__ err) {
+  __shared__ uint64_t s[kBT];
+  const int t = blockIdx.x;
+  const uint32_t* c = hist + (size_t)t * EP_HIST_BINS;
+  uint16_t* f = out->freq + (size_t)t * EP_HIST_BINS;
+
+  // span, total and number of distinct values
+  uint32_t first = 0xFFFFFFFFu, last = 0, distinct = 0;
+  uint64_t total = 0;
+  for (uint32_t b = threadIdx.x; b < EP_HIST_BINS; b += kBT) {
+    const uint32_t v = c[b];
+    if (v) {
+      first = b < first ? b : first;
+      last = b;
+      total += v;
+      distinct++;
+    }
+  }
+  first = 0xFFFFFFFFu - (uint32_t)block_max_u64(0xFFFFFFFFu - first, s);
+  last = (uint32_t)block_max_u64(distinct ? last : 0u, s);
+  total = block_sum_u64(total, s);
+  distinct = (uint32_t)block_sum_u64(distinct, s);
+  if (distinct == 0) {
+    if (threadIdx.x == 0) {
+      out->lo[t] = 0;
+      out->n[t] = 0;
+    }
+    return;
+  }
+  if (distinct > kNormM) {
+    if (threadIdx.x == 0) atomicOr(err, 1u << EP_ERR_ALPHABET);
+    return;
+  }
+  const uint32_t n = last - first + 1u;
+  if (threadIdx.x == 0) {
+    out->lo[t] = (int32_t)first - 32768;
+    out->n[t] = n;
+  }
+
+  // first frequencies, their sum, and the most frequent value (lowest index on ties)
+  uint64_t assigned = 0, top_cnt = 0;
+  for (uint32_t i = threadIdx.x; i < n; i += kBT) {
+    const uint32_t v = c[first + i];
+    uint32_t q = 0;
+    if (v) {
+      q = (uint32_t)(((uint64_t)v * kNormM) / total);
+      q = q < 1u ? 1u : q;
+    }
+    f[i] = (uint16_t)q;
+    assigned += q;
+    const uint64_t key = ((uint64_t)v << 32) | (0xFFFFFFFFu - i);
+    top_cnt = key > top_cnt ? key : top_cnt;
+  }
+  assigned = block_sum_u64(assigned, s);
+  top_cnt = block_max_u64(top_cnt, s);
+  int64_t gap = (int64_t)kNormM - (int64_t)assigned;
+  if (gap > 0) {
+    if (threadIdx.x == 0) {
+      const uint32_t i = 0xFFFFFFFFu - (uint32_t)top_cnt;
+      f[i] = (uint16_t)(f[i] + gap);
+    }
+    return;
+  }
+  // excess: repeatedly the largest frequency above 1 (lowest index on ties) gives up what it can
+  while (gap < 0) {
+    uint64_t key = 0;
+    for (uint32_t i = threadIdx.x; i < n; i += kBT) {
+      const uint32_t q = f[i];
+      const uint64_t k = q > 1u ? (((uint64_t)q << 32) | (0xFFFFFFFFu - i)) : 0u;
+      key = k > key ? k : key;
+    }
+    key = block_max_u64(key, s);                  // (ends with a barrier: every f[] read done)
+    if (key == 0) break;                          // (cannot happen: distinct <= 2^P)
+    const uint32_t i = 0xFFFFFFFFu - (uint32_t)key;
+    const int64_t q = (int64_t)(key >> 32);
+    const int64_t take = -gap < q - 1 ? -gap : q - 1;
+    if (threadIdx.x == 0) f[i] = (uint16_t)(q - take);
+    gap += take;
+    __syncthreads();                              // the update before the next scan
+  }
+}
+
+// Sum over tables t, then values i < n[t] with a nonzero count, of count * cost[freq], left to
+// right, each product and each sum rounded separately (one wavefront; lanes load 64 values at a
+// time, the sum walks them in order).  The addends are >= 0 and the sum starts at +0, so the
+// values skipped (count 0) would add exactly nothing.
+__global__ __launch_bounds__(64) void k_sum_bits(const uint32_t* __restrict__ hist,
+                                                 const ep_tables* __restrict__ tab,
+                                                 const double* __restrict__ cost,
+                                                 const uint32_t* __restrict__ err,
+                                                 double* __restrict__ bits) {
+  const int lane = threadIdx.x;
+  if (*err & (1u << EP_ERR_ALPHABET)) {
+    if (lane == 0) *bits = 0.0;
+    return;
+  }
+  double acc = 0.0;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    const uint32_t n = tab->n[t];
+    const uint32_t* c = hist + (size_t)t * EP_HIST_BINS + (tab->lo[t] + 32768);
+    const uint16_t* fq = tab->freq + (size_t)t * EP_HIST_BINS;
+    for (uint32_t b = 0; b < n; b += 64) {
+      const uint32_t i = b + lane;
+      const uint32_t v = i < n ? c[i] : 0u;
+      double p = 0.0;
+      if (v) p = __dmul_rn((double)v, cost[fq[i]]);
+      uint64_t m = __ballot(v != 0u);
+      while (m) {
+        const int k = __builtin_ctzll(m);
+        m &= m - 1;
+        const uint64_t pb = __double_as_longlong(p);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, k);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), k);
+        acc = __dadd_rn(acc, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+      }
+    }
+  }
+  if (lane == 0) *bits = acc;
+}
+
+// P - log2(f) for f = 1 .. 2^P (entry 0 unused), with the host's log2.
+static const std::array<double, kNormM + 1>& cost_table() {
+  static const std::array<double, kNormM + 1> tab = [] {
+    std::array<double, kNormM + 1> a{};
+    for (uint32_t f = 1; f <= kNormM; f++) a[f] = (double)EP_PRECISION - std::log2((double)f);
+    return a;
+  }();
+  return tab;
+}
+
+// Workspace of the device estimate: tables, cost table, bit sum + error word.
+struct RateWs {
+  ep_tables* tables;
+  double* cost;
+  double* bits;
+  uint32_t* err;
+  size_t total;
+};
+
+static RateWs rate_carve(void* base) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t o = 0;
+  RateWs w;
+  w.tables = reinterpret_cast<ep_tables*>(p + o); o += up(sizeof(ep_tables));
+  w.cost = reinterpret_cast<double*>(p + o); o += up(8 * (size_t)(kNormM + 1));
+  w.bits = reinterpret_cast<double*>(p + o); o += up(8);
+  w.err = reinterpret_cast<uint32_t*>(p + o); o += up(4);
+  w.total = o;
+  return w;
+}
+
+__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+
+}  // namespace ep
+
+using namespace ep;
+
+extern "C" ep_status ep_build_tables_gpu(const ep_hist* d_hist, ep_tables* d_out, uint32_t* d_err,
+                                         void* stream) {
+  if (!d_hist || !d_out || !d_err) return EP_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  k_build_tables<<<EP_NTABLES, kBT, 0, s>>>(d_hist->counts, d_out, d_err);
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+extern "C" size_t ep_estimate_workspace_bytes(void) { return rate_carve(nullptr).total; }
+
+// Internal: the device part of the estimate, enqueued on `s`; the sum of bits lands in
+// h_bits and the table sizes in h_n after the stream synchronises.  Returns false on a HIP error.
+namespace ep {
+bool estimate_enqueue(const ep_hist* d_hist, void* d_workspace, bool upload_cost, hipStream_t s,
+                      double* h_bits, uint32_t* h_err, uint32_t* h_n) {
+  const RateWs w = rate_carve(d_workspace);
+  bool ok = true;
+  if (upload_cost)
+    ok &= hipMemcpyAsync(w.cost, cost_table().data(), 8 * (size_t)(kNormM + 1),
+                         hipMemcpyHostToDevice, s) == hipSuccess;
+  k_zero_u32<<<1, 1, 0, s>>>(w.err);
+  k_build_tables<<<EP_NTABLES, kBT, 0, s>>>(d_hist->counts, w.tables, w.err);
+  k_sum_bits<<<1, 64, 0, s>>>(d_hist->counts, w.tables, w.cost, w.err, w.bits);
+  ok &= hipGetLastError() == hipSuccess;
+  ok &= hipMemcpyAsync(h_bits, w.bits, 8, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok &= hipMemcpyAsync(h_err, w.err, 4, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok &= hipMemcpyAsync(h_n, w.tables->n, 4 * EP_NTABLES, hipMemcpyDeviceToHost, s) == hipSuccess;
+  return ok;
+}
+
+const ep_tables* estimate_tables(void* d_workspace) { return rate_carve(d_workspace).tables; }
+}  // namespace ep
