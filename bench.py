@@ -68,10 +68,16 @@ def main():
     t = torch.from_numpy(w_bits.view(np.uint8)).to(dev).view(tdt).view(R, C)
     n_mat = 64 if key == 4 else 1
 
-    # compress once (library: GPU rate search, quantiser, histogram, LS scales; host encoder)
+    # compress (library: device rate search, quantiser, histogram, LS scales, tables, tile
+    # encoder); the second call is the warm time
     t0 = time.time()
     comp = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F))
     compress_s = time.time() - t0
+    t0 = time.time()
+    comp2 = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F))
+    compress_warm_s = time.time() - t0
+    assert np.array_equal(comp.blob, comp2.blob)
+    del comp2
     info = comp.info
     blob_bytes = int(comp.blob.size)
     out_bytes = R * C * esize
@@ -131,6 +137,35 @@ def main():
     torch.cuda.synchronize()
     q_ms = ev0.elapsed_time(ev1) / qsteps
     q_bytes = R * C * esize + R * C // 8 + R * C * 2    # read weights, write cosets + fields
+
+    # device tile encoder on those symbols (tables built on the device, as compress does)
+    nv = R * C // 8
+    d_tab = torch.empty(ep.TABLES_BYTES, dtype=torch.uint8, device=dev)
+    assert ep.ep_build_tables_gpu(hist, d_tab, qerr) == 0
+    h_tab = d_tab.cpu().numpy()
+    ews = ep.ep_encode_workspace_bytes(nv, F)
+    d_ews = torch.empty(ews, dtype=torch.uint8, device=dev)
+    T = (nv + F // 8 - 1) // (F // 8)
+    d_woff = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    d_max = torch.empty(1, dtype=torch.int32, device=dev)
+    d_st = torch.empty(T * 64, dtype=torch.int32, device=dev)
+    d_words = torch.empty(9 * nv + 1, dtype=torch.int16, device=dev)
+
+    def enc():
+        assert ep.ep_encode_tiles_gpu(cos, fld, nv, F, h_tab, d_ews, ews, d_woff, d_max, d_st,
+                                      d_words, 9 * nv + 1, qerr) == 0
+
+    for _ in range(3):
+        enc()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(qsteps):
+        enc()
+    ev1.record()
+    torch.cuda.synchronize()
+    e_ms = ev0.elapsed_time(ev1) / qsteps
+    assert int(qerr.item()) == 0
+    assert int(d_woff[-1].item()) == info.payload_words
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -198,6 +233,7 @@ def main():
             "blob_bytes": blob_bytes, "output_bytes": out_bytes,
             "rotated_copies": ROTATE if n_mat == 1 else 0, "matrices": n_mat,
             "compress_seconds": round(compress_s, 3),
+            "compress_seconds_warm": round(compress_warm_s, 3),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -212,13 +248,18 @@ def main():
             "achieved_GBs": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
             "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
+        "encode": {
+            "kernel": f"k_encode_tiles<{F // 512}> + offset scan + word copy",
+            "ms": round(e_ms, 6), "vectors": nv,
+            "Mvectors_per_s": round(nv / (e_ms * 1e-3) / 1e6, 1),
+        },
     }
     if single is not None:
         line["config"]["workload"] = wl["name"] + f", target {target} bpp, {F}-field tiles, " \
             f"all {n_mat} matrices decoded by one batched call per step"
         line["config"].update(single)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(comp.blob, out_bytes, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(comp.blob, R * C * esize, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
@@ -261,7 +302,7 @@ def cpu_baseline(blob, out_bytes, min_seconds):
     return {
         "value": round(out_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
         "kind": "oracle",
-        "sample": f"whole 4096x4096 blob decoded {reps} times in {el:.1f} s (single thread)",
+        "sample": f"whole blob decoded {reps} times in {el:.1f} s (single thread)",
     }
 
 
