@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ep.h"
 #include "ep_device.h"
@@ -22,40 +23,71 @@ namespace ep {
 
 // ------------------------------------------------------------------------------------------
 // Row sums of squares: one lane per row, left-to-right fp64 accumulation (each square is exact
-// in fp64 for every container, so the sum is reproducible).  A 64-row x 64-column tile is
-// staged through LDS so the global reads are row-contiguous.
+// in fp64 for every container, so the sum is reproducible).  The chain is serial per row, so a
+// lane streams its own row: the next chunk of kRowChunk vectors is loaded (8- or 16-byte loads)
+// while the current one is summed, which keeps the loads off the chain's critical path.
 // ------------------------------------------------------------------------------------------
+constexpr int kRowChunk = 8;                       // vectors per lane per prefetch stage
+
+template <int DT>
+struct RawVec {                                    // the 8 container values of one vector
+  using T = typename std::conditional<(DT == EP_BF16 || DT == EP_FP16), uint4, uint2>::type;
+};
+
+template <int DT>
+__device__ __forceinline__ typename RawVec<DT>::T raw_load(const void* base, int64_t vec) {
+  return reinterpret_cast<const typename RawVec<DT>::T*>(base)[vec];
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_widen(const typename RawVec<DT>::T& q, float out[8]) {
+  if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      out[2 * i] = widen<DT>(w[i] & 0xFFFFu);
+      out[2 * i + 1] = widen<DT>(w[i] >> 16);
+    }
+  } else {
+    const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = widen<DT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, int64_t rows,
                                                   int64_t cols, double* __restrict__ out) {
-  __shared__ float tile[64][65];
-  const int lane = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  using Raw = typename RawVec<DT>::T;
+  const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (r >= rows) return;
+  const int64_t vpr = cols / 8, v_row = r * vpr;
+  Raw cur[kRowChunk], nxt[kRowChunk];
+#pragma unroll
+  for (int k = 0; k < kRowChunk; k++)
+    if (k < vpr) cur[k] = raw_load<DT>(w, v_row + k);
   double acc = 0.0;
-  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
-    const int64_t nc = (cols - c0 < 64) ? cols - c0 : 64;
-    for (int rr = 0; rr < 64; rr++) {
-      const int64_t r = r0 + rr;
-      float v = 0.0f;
-      if (r < rows && lane < nc) {
-        const int64_t i = r * cols + c0 + lane;
-        uint32_t bits = (DT == EP_BF16 || DT == EP_FP16)
-                            ? (uint32_t)static_cast<const uint16_t*>(w)[i]
-                            : (uint32_t)static_cast<const uint8_t*>(w)[i];
-        v = widen<DT>(bits);
-      }
-      tile[rr][lane] = v;
-    }
-    __syncthreads();
-    if (r0 + lane < rows) {
-      for (int cc = 0; cc < nc; cc++) {
-        double v = (double)tile[lane][cc];
-        acc = __dadd_rn(acc, __dmul_rn(v, v));
+  for (int64_t v0 = 0; v0 < vpr; v0 += kRowChunk) {
+    const int64_t v1 = v0 + kRowChunk;
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++)
+      if (v1 + k < vpr) nxt[k] = raw_load<DT>(w, v_row + v1 + k);
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++) {
+      if (v0 + k < vpr) {
+        float x[8];
+        raw_widen<DT>(cur[k], x);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const double v = (double)x[i];
+          acc = __dadd_rn(acc, __dmul_rn(v, v));
+        }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++) cur[k] = nxt[k];
   }
-  if (r0 + lane < rows) out[r0 + lane] = acc;
+  out[r] = acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -295,7 +327,8 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
 }
 
 // ------------------------------------------------------------------------------------------
-// Row least-squares terms: one lane per row; 64 rows x 64 columns (8 vectors) per LDS stage.
+// Row least-squares terms: one lane per row, streamed like the row sums (weights, fields and
+// cosets of the next kRowChunk vectors loaded while the current ones are summed).
 // num = sum w * p (fp64, left to right; each product exact), den4 = sum (2p)^2 (int64).
 // ------------------------------------------------------------------------------------------
 template <int DT>
@@ -304,54 +337,69 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
                                                 const int16_t* __restrict__ fields,
                                                 double* __restrict__ num,
                                                 int64_t* __restrict__ den4) {
-  __shared__ float sw[64][65];
-  __shared__ int16_t sf[64][66];
-  __shared__ uint8_t sc[64][9];
-  const int lane = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int64_t vpr = cols / 8;
+  using Raw = typename RawVec<DT>::T;
+  const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (r >= rows) return;
+  const int64_t vpr = cols / 8, v_row = r * vpr;
+  const uint4* fv = reinterpret_cast<const uint4*>(fields);
+  Raw cw[kRowChunk], nw[kRowChunk];
+  uint4 cf[kRowChunk], nf[kRowChunk];
+  uint32_t cc[kRowChunk], nc[kRowChunk];
+#pragma unroll
+  for (int k = 0; k < kRowChunk; k++) {
+    if (k < vpr) {
+      cw[k] = raw_load<DT>(w, v_row + k);
+      cf[k] = fv[v_row + k];
+      cc[k] = coset[v_row + k];
+    }
+  }
   double acc = 0.0;
   int64_t d4 = 0;
-  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
-    const int64_t nc = (cols - c0 < 64) ? cols - c0 : 64;
-    for (int rr = 0; rr < 64; rr++) {
-      const int64_t r = r0 + rr;
-      float v = 0.0f;
-      int16_t f = 0;
-      if (r < rows && lane < nc) {
-        const int64_t i = r * cols + c0 + lane;
-        uint32_t bits = (DT == EP_BF16 || DT == EP_FP16)
-                            ? (uint32_t)static_cast<const uint16_t*>(w)[i]
-                            : (uint32_t)static_cast<const uint8_t*>(w)[i];
-        v = widen<DT>(bits);
-        f = fields[i];
+  for (int64_t v0 = 0; v0 < vpr; v0 += kRowChunk) {
+    const int64_t v1 = v0 + kRowChunk;
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++) {
+      if (v1 + k < vpr) {
+        nw[k] = raw_load<DT>(w, v_row + v1 + k);
+        nf[k] = fv[v_row + v1 + k];
+        nc[k] = coset[v_row + v1 + k];
       }
-      sw[rr][lane] = v;
-      sf[rr][lane] = f;
-      if (lane < 8) sc[rr][lane] = (r < rows && lane < nc / 8) ? coset[r * vpr + c0 / 8 + lane] : 0;
     }
-    __syncthreads();
-    if (r0 + lane < rows) {
-      for (int m = 0; m < nc / 8; m++) {
-        const int32_t c = sc[lane][m];
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++) {
+      if (v0 + k < vpr) {
+        float x[8];
+        raw_widen<DT>(cw[k], x);
+        const uint32_t q[4] = {cf[k].x, cf[k].y, cf[k].z, cf[k].w};
+        int32_t f[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          f[2 * i] = (int32_t)(int16_t)(q[i] & 0xFFFFu);
+          f[2 * i + 1] = (int32_t)q[i] >> 16;
+        }
         int32_t par = 0;
-        for (int k = 0; k < 7; k++) par ^= sf[lane][8 * m + k];
-        for (int k = 0; k < 8; k++) {
-          int32_t z = sf[lane][8 * m + k];
-          if (k == 7) z = 2 * z + (par & 1);
-          const int64_t h = 2 * (int64_t)z + c;
+#pragma unroll
+        for (int i = 0; i < 7; i++) par ^= f[i];
+        f[7] = 2 * f[7] + (par & 1);
+        const int32_t c = (int32_t)cc[k];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int64_t h = 2 * (int64_t)f[i] + c;
           const double p = (double)h * 0.5;
-          acc = __dadd_rn(acc, __dmul_rn((double)sw[lane][8 * m + k], p));
+          acc = __dadd_rn(acc, __dmul_rn((double)x[i], p));
           d4 += h * h;
         }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRowChunk; k++) {
+      cw[k] = nw[k];
+      cf[k] = nf[k];
+      cc[k] = nc[k];
+    }
   }
-  if (r0 + lane < rows) {
-    num[r0 + lane] = acc;
-    den4[r0 + lane] = d4;
-  }
+  num[r] = acc;
+  den4[r] = d4;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -411,6 +459,7 @@ static bool valid_dtype(int32_t dt) { return dt >= EP_BF16 && dt <= EP_INT8; }
 extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
                                   double* d_out, void* stream) {
   if (!d_w || !d_out) return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_w) & 15u) return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
   if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -467,6 +516,8 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
                                 const uint8_t* d_coset, const int16_t* d_fields, double* d_num,
                                 int64_t* d_den4, void* stream) {
   if (!d_w || !d_coset || !d_fields || !d_num || !d_den4) return EP_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
+    return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
   if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
