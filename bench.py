@@ -264,12 +264,18 @@ def main():
 
 
 def decoder_source_sha() -> str:
+    """Hash of the decoder's code (comments and blank space removed, so that a comment edit
+    does not invalidate the counter record)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "entropy_coded_weight_ep_amd", "csrc")
     for f in ("ep_decode.h", "ep_device.h", "ep_internal.h"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        src = open(os.path.join(csrc, f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

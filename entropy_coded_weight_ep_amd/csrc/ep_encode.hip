@@ -1,8 +1,8 @@
 // GPU tile encoder (gfx950): the interleaved 64-state rANS encoding of the coset and field
 // symbols, tile by tile, producing the blob's tile offsets, final states and word stream.
 //
-// "The selected fields are encoded with rANS in independently decodable tiles" (EntroPack design
-// page, "Encoding and reconstruction"; rANS after Duda, "Asymmetric numeral systems", 2009; the
+// The fields are rANS-coded in tiles that each decode on their own (EntroPack design page,
+// "Encoding and reconstruction"; rANS after Duda, "Asymmetric numeral systems", 2009; the
 // interleaving after Giesen, "Interleaved entropy coders", 2014).  The word order is the
 // decoder's: phases (coset, field 0..7), inside each the lane's vectors ascending, inside that the
 // lanes ascending.  The encoder walks that order backwards, so every tile's stream is the reverse
