@@ -98,9 +98,14 @@ def widen(bits: np.ndarray, dtype: int) -> np.ndarray:
     return out.reshape(bits.shape)
 
 
+def bits_dtype(dtype: int):
+    """numpy type of a container's raw bits."""
+    return {1: np.uint16, 2: np.uint16, 3: np.uint8, 4: np.int8, 5: np.uint32}[dtype]
+
+
 def narrow(values: np.ndarray, dtype: int) -> np.ndarray:
     v = np.ascontiguousarray(values, np.float32)
-    out = np.empty(v.size, np.uint16 if dtype in (1, 2) else (np.uint8 if dtype == 3 else np.int8))
+    out = np.empty(v.size, bits_dtype(dtype))
     lib().or_narrow_array(dtype, _p(v), v.size, _p(out))
     return out.reshape(v.shape)
 
@@ -266,7 +271,7 @@ def decompress(blob: np.ndarray, t0: int = 0, t1: int = -1, want_fields: bool = 
     """Returns (status, out container bits [R, C], coset, fields)."""
     info = blob_fields(blob)
     R, Cc, dt = info["rows"], info["cols"], info["dtype"]
-    out = np.zeros((R, Cc), np.uint16 if dt in (1, 2) else (np.uint8 if dt == 3 else np.int8))
+    out = np.zeros((R, Cc), bits_dtype(dt))
     nv = R * Cc // 8
     cos = np.zeros(nv, np.uint8) if want_fields else None
     fld = np.zeros(nv * 8, np.int16) if want_fields else None

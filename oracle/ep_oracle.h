@@ -26,7 +26,7 @@ enum {
   OR_ERR_RANGE = 5, OR_ERR_ALPHABET = 6, OR_ERR_CORRUPT = 7, OR_ERR_VERSION = 8,
   OR_ERR_CAPACITY = 10
 };
-enum { OR_BF16 = 1, OR_FP16 = 2, OR_FP8 = 3, OR_INT8 = 4 };
+enum { OR_BF16 = 1, OR_FP16 = 2, OR_FP8 = 3, OR_INT8 = 4, OR_FP32 = 5 };
 
 #define OR_NTABLES 17
 #define OR_NBINS 65536 /* histogram bins per table: value + 32768 */

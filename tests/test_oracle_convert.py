@@ -118,3 +118,18 @@ def test_narrow_exhaustive_all_fp32(orc, dt):
         if dt == S.FP8:
             ok &= np.abs(x.astype(np.float64)) < 464.0
         assert np.array_equal(got[ok], ref[ok])
+
+
+def test_fp32_container_keeps_every_value(orc, pats):
+    """The fp32 container (a reading beyond the abstract's list) stores the fp32 value itself:
+    widening and narrowing are the identity on every non-NaN pattern, subnormals and infinities
+    included; NaN stays NaN."""
+    bits = pats.view(np.uint32)
+    fin = ~np.isnan(pats)
+    got = orc.widen(bits, S.FP32)
+    assert np.array_equal(got[fin].view(np.uint32), bits[fin])
+    assert np.all(np.isnan(got[~fin]))
+    back = orc.narrow(pats, S.FP32)
+    assert back.dtype == np.uint32
+    assert np.array_equal(back[fin], bits[fin])
+    assert np.all(np.isnan(back[~fin][:1000].view(np.float32)))
