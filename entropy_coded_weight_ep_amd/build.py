@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libep.so")
 UNITS = ["ep_kernels.hip", "ep_decode_bf16.hip", "ep_decode_fp16.hip", "ep_decode_fp8.hip",
-         "ep_decode_int8.hip", "ep_encode.hip", "ep_rate.hip", "ep_host.cpp"]
+         "ep_decode_int8.hip", "ep_decode_fp32.hip", "ep_encode.hip", "ep_rate.hip", "ep_host.cpp"]
 SOURCES = [os.path.join(CSRC, u) for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "ep.h")] + [
     os.path.join(CSRC, h) for h in ("ep_internal.h", "ep_device.h", "ep_decode.h")]

@@ -1,0 +1,7 @@
+// Fused tile decoder instantiated for the fp32 container (kernels in ep_decode.h).
+#include "ep_decode.h"
+
+namespace ep {
+template hipError_t launch_decode<EP_FP32>(const DecodeArgs&, int, bool, bool, bool, bool,
+                                           int, size_t, hipStream_t);
+}  // namespace ep

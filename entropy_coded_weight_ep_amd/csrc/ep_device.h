@@ -1,10 +1,12 @@
 // Device-side helpers shared by the HIP translation units of libep.so: rANS constants and the
 // container conversions (BF16, FP16, FP8 E4M3FN and INT8 containers, as the EntroPack abstract
-// lists them).  Conversions to a container round to nearest even; E4M3FN saturates at +-448,
-// INT8 saturates at [-128, 127].
+// lists them, and FP32).  Conversions to a container round to nearest even; E4M3FN saturates at
+// +-448, INT8 saturates at [-128, 127]; FP32 is stored as is.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ep.h"
 
@@ -35,8 +37,56 @@ __device__ __forceinline__ float widen(uint32_t bits) {
     return (float)h;
   } else if constexpr (DT == EP_FP8_E4M3FN) {
     return fp8e4m3_to_f32(bits);
+  } else if constexpr (DT == EP_FP32) {
+    return __uint_as_float(bits);
   } else {
     return (float)(int8_t)(uint8_t)bits;
+  }
+}
+
+// The 8 container values of one vector as loaded from memory: 32 bytes (fp32), 16 bytes (bf16,
+// fp16) or 8 bytes (fp8, int8).  A vector starts at element 8m of a row whose length is a
+// multiple of 8, so its load is aligned whenever the tensor is 16-byte aligned.
+struct U32x8 {
+  uint4 a, b;
+};
+
+template <int DT>
+struct RawVec {
+  using T = typename std::conditional<
+      DT == EP_FP32, U32x8,
+      typename std::conditional<(DT == EP_BF16 || DT == EP_FP16), uint4, uint2>::type>::type;
+};
+
+template <int DT>
+__device__ __forceinline__ typename RawVec<DT>::T raw_load(const void* base, int64_t vec) {
+  return reinterpret_cast<const typename RawVec<DT>::T*>(base)[vec];
+}
+
+template <int DT>
+__device__ __forceinline__ typename RawVec<DT>::T raw_zero() {
+  typename RawVec<DT>::T z;
+  __builtin_memset(&z, 0, sizeof(z));
+  return z;
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_widen(const typename RawVec<DT>::T& q, float out[8]) {
+  if constexpr (DT == EP_FP32) {
+    const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = __uint_as_float(w[i]);
+  } else if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      out[2 * i] = widen<DT>(w[i] & 0xFFFFu);
+      out[2 * i + 1] = widen<DT>(w[i] >> 16);
+    }
+  } else {
+    const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = widen<DT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
   }
 }
 
@@ -60,24 +110,6 @@ __device__ __forceinline__ uint32_t narrow2(float a, float b) {
   } else {
     typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h16x2));
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t elem, float out[8]) {
-  if constexpr (DT == EP_BF16 || DT == EP_FP16) {
-    uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      out[2 * i] = widen<DT>(w[i] & 0xFFFFu);
-      out[2 * i + 1] = widen<DT>(w[i] >> 16);
-    }
-  } else {
-    uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + elem);
-    uint32_t w[2] = {q.x, q.y};
-#pragma unroll
-    for (int i = 0; i < 8; i++) out[i] = widen<DT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
   }
 }
 

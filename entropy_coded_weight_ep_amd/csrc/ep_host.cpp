@@ -405,7 +405,7 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   std::memcpy(&I.scale, b + 40, 8);
   std::memcpy(&u64, b + 48, 8); I.payload_words = (int64_t)u64;
   std::memcpy(&I.max_tile_words, b + 56, 4);
-  if (I.dtype < EP_BF16 || I.dtype > EP_INT8) return EP_ERR_DTYPE;
+  if (I.dtype < EP_BF16 || I.dtype > EP_FP32) return EP_ERR_DTYPE;
   if (I.precision != EP_PRECISION || I.lanes != EP_LANES) return EP_ERR_VERSION;
   if (I.rows < 1 || I.cols < 8 || I.cols % 8 || I.tile_fields < 512 || I.tile_fields % 512)
     return EP_ERR_CORRUPT;
@@ -482,7 +482,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
                                  void* h_blob, size_t cap, size_t* out_bytes, double* scale_out,
                                  void* stream) {
   if (!d_w || !cfg || !d_workspace || !h_blob || !out_bytes) return EP_ERR_ARG;
-  if (dtype < EP_BF16 || dtype > EP_INT8) return EP_ERR_DTYPE;
+  if (dtype < EP_BF16 || dtype > EP_FP32) return EP_ERR_DTYPE;
   if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
   const uint32_t F = cfg->tile_fields;
   if (F < 512 || F % 512) return EP_ERR_ARG;

@@ -30,32 +30,6 @@ namespace ep {
 constexpr int kRowChunk = 8;                       // vectors per lane per prefetch stage
 
 template <int DT>
-struct RawVec {                                    // the 8 container values of one vector
-  using T = typename std::conditional<(DT == EP_BF16 || DT == EP_FP16), uint4, uint2>::type;
-};
-
-template <int DT>
-__device__ __forceinline__ typename RawVec<DT>::T raw_load(const void* base, int64_t vec) {
-  return reinterpret_cast<const typename RawVec<DT>::T*>(base)[vec];
-}
-
-template <int DT>
-__device__ __forceinline__ void raw_widen(const typename RawVec<DT>::T& q, float out[8]) {
-  if constexpr (DT == EP_BF16 || DT == EP_FP16) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      out[2 * i] = widen<DT>(w[i] & 0xFFFFu);
-      out[2 * i + 1] = widen<DT>(w[i] >> 16);
-    }
-  } else {
-    const uint32_t w[2] = {q.x, q.y};
-#pragma unroll
-    for (int i = 0; i < 8; i++) out[i] = widen<DT>((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-  }
-}
-
-template <int DT>
 __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, int64_t rows,
                                                   int64_t cols, double* __restrict__ out) {
   using Raw = typename RawVec<DT>::T;
@@ -161,20 +135,21 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int6
     p[i] = v;
 }
 
-// One vector's input, fetched one iteration ahead of its use: raw container bits (16 bytes for
-// 16-bit containers, 8 for 8-bit ones), the row gain, and whether the row index was valid.
+// One vector's input, fetched one iteration ahead of its use: raw container bits, the row gain,
+// and whether the row index was valid.
+template <int DT>
 struct QIn {
-  uint4 raw;
+  typename RawVec<DT>::T raw;
   float g;
   bool ok;
 };
 
 template <int DT>
-__device__ __forceinline__ QIn q_fetch(const void* __restrict__ w, int64_t rows, int64_t cols,
-                                       const float* __restrict__ gain,
-                                       const int64_t* __restrict__ row_index, uint32_t v,
-                                       uint32_t vpr, double inv_vpr) {
-  QIn q;
+__device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t rows,
+                                           int64_t cols, const float* __restrict__ gain,
+                                           const int64_t* __restrict__ row_index, uint32_t v,
+                                           uint32_t vpr, double inv_vpr) {
+  QIn<DT> q;
   // i = v / vpr: fp64 estimate, then one exact correction
   uint32_t i = (uint32_t)((double)v * inv_vpr);
   const int64_t rem = (int64_t)v - (int64_t)i * vpr;
@@ -182,36 +157,13 @@ __device__ __forceinline__ QIn q_fetch(const void* __restrict__ w, int64_t rows,
   const uint32_t m = v - i * vpr;
   const int64_t r = row_index ? row_index[i] : (int64_t)i;
   q.ok = r >= 0 && r < rows;
-  q.raw = make_uint4(0, 0, 0, 0);
+  q.raw = raw_zero<DT>();
   q.g = 0.0f;
   if (q.ok) {
-    const int64_t e = r * cols + 8 * (int64_t)m;
-    if constexpr (DT == EP_BF16 || DT == EP_FP16) {
-      q.raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + e);
-    } else {
-      const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(w) + e);
-      q.raw.x = h.x;
-      q.raw.y = h.y;
-    }
+    q.raw = raw_load<DT>(w, r * (cols / 8) + (int64_t)m);
     q.g = gain[r];
   }
   return q;
-}
-
-template <int DT>
-__device__ __forceinline__ void q_widen(const uint4& raw, float x[8]) {
-  if constexpr (DT == EP_BF16 || DT == EP_FP16) {
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      x[2 * i] = widen<DT>(w4[i] & 0xFFFFu);
-      x[2 * i + 1] = widen<DT>(w4[i] >> 16);
-    }
-  } else {
-    const uint32_t w2[2] = {raw.x, raw.y};
-#pragma unroll
-    for (int i = 0; i < 8; i++) x[i] = widen<DT>((w2[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-  }
 }
 
 // E8 quantiser + fused per-(coset, field) histogram.  A workgroup of 16 wavefronts walks the
@@ -239,17 +191,17 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
   uint32_t n_c0 = 0, n_c1 = 0;
   const uint32_t stride = gridDim.x * (uint32_t)kQThreads;
   uint32_t v = blockIdx.x * (uint32_t)kQThreads + threadIdx.x;
-  QIn cur;
+  QIn<DT> cur;
   if (v < n_vec) cur = q_fetch<DT>(w, rows, cols, gain, row_index, v, vpr, inv_vpr);
   for (; v < n_vec; v += stride) {
-    QIn nxt;
+    QIn<DT> nxt;
     const bool more = v + stride < n_vec;         // (no overflow: n_vec + stride < 2^32)
     if (more) nxt = q_fetch<DT>(w, rows, cols, gain, row_index, v + stride, vpr, inv_vpr);
     if (!cur.ok) {                                // a row index outside the tensor: skip, report
       bad_row = true;
     } else {
       float x[8];
-      q_widen<DT>(cur.raw, x);
+      raw_widen<DT>(cur.raw, x);
       bool out_of_range = false;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
@@ -454,7 +406,7 @@ __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict
 // ==========================================================================================
 using namespace ep;
 
-static bool valid_dtype(int32_t dt) { return dt >= EP_BF16 && dt <= EP_INT8; }
+static bool valid_dtype(int32_t dt) { return dt >= EP_BF16 && dt <= EP_FP32; }
 
 extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
                                   double* d_out, void* stream) {
@@ -468,6 +420,7 @@ extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, 
     case EP_BF16: k_row_sumsq<EP_BF16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
     case EP_FP16: k_row_sumsq<EP_FP16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
     case EP_FP8_E4M3FN: k_row_sumsq<EP_FP8_E4M3FN><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+    case EP_FP32: k_row_sumsq<EP_FP32><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
     default: k_row_sumsq<EP_INT8><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
   }
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
@@ -506,6 +459,7 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
     case EP_BF16: EP_Q(EP_BF16); break;
     case EP_FP16: EP_Q(EP_FP16); break;
     case EP_FP8_E4M3FN: EP_Q(EP_FP8_E4M3FN); break;
+    case EP_FP32: EP_Q(EP_FP32); break;
     default: EP_Q(EP_INT8); break;
   }
 #undef EP_Q
@@ -527,6 +481,7 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
     case EP_BF16: EP_L(EP_BF16); break;
     case EP_FP16: EP_L(EP_FP16); break;
     case EP_FP8_E4M3FN: EP_L(EP_FP8_E4M3FN); break;
+    case EP_FP32: EP_L(EP_FP32); break;
     default: EP_L(EP_INT8); break;
   }
 #undef EP_L
@@ -559,7 +514,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   if ((flags & ~layout) || (layout & (layout - 1u))) return EP_ERR_ARG;
   if (n < 1 || !d_blobs || !infos || !d_dec_tables || !d_outs || !d_err) return EP_ERR_ARG;
   const ep_blob_info& i0 = infos[0];
-  if (i0.dtype < EP_BF16 || i0.dtype > EP_INT8) return EP_ERR_DTYPE;
+  if (!valid_dtype(i0.dtype)) return EP_ERR_DTYPE;
   const int J = i0.tile_fields / (8 * EP_LANES);
   if (i0.tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
   // batch-wide choices: the largest tile, any wide alphabet, any tiny row scale
@@ -640,13 +595,15 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       case EP_FP8_E4M3FN:
         e = launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, ring, waves, lds, s);
         break;
+      case EP_FP32: e = launch_decode<EP_FP32>(a, J, big, ragged, slow, ring, waves, lds, s); break;
       default: e = launch_decode<EP_INT8>(a, J, big, ragged, false, ring, waves, lds, s); break;
     }
     a.n = 0;
     return e == hipSuccess ? EP_OK : EP_ERR_HIP;
   };
   // the fused scaling is exact for fp16, fp8 and int8 whatever the scales (a tiny scale's products
-  // round to zero in those containers); bf16 keeps the subnormal range and needs the exact half
+  // round to zero in those containers); bf16 and fp32 keep the subnormal range and need the exact
+  // half
   for (int pass = 0; pass < 2; pass++) {             // full tiles, then ragged last tiles
     const bool ragged = pass == 1;
     a.n = 0;

@@ -98,7 +98,7 @@ class GpuBlob:
         assert ep.ep_prepare_decode(self.d_blob, self.info, self.d_tab) == 0
 
     def out_bytes(self):
-        esize = 2 if self.info.dtype in (1, 2) else 1
+        esize = {1: 2, 2: 2, 3: 1, 4: 1, 5: 4}[self.info.dtype]
         return self.info.rows * self.info.cols * esize
 
     def decode(self, d_out=None, flags=None):
@@ -118,7 +118,7 @@ class GpuBlob:
         torch.cuda.synchronize()
         out = host(d_out)
         dt = self.info.dtype
-        npdt = np.uint16 if dt in (1, 2) else (np.uint8 if dt == 3 else np.int8)
+        npdt = {1: np.uint16, 2: np.uint16, 3: np.uint8, 4: np.int8, 5: np.uint32}[dt]
         return int(host(d_err)[0]), out.view(npdt).reshape(self.info.rows, self.info.cols)
 
 
@@ -128,7 +128,8 @@ def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
     import torch
 
     ep = ep_mod()
-    tmap = {1: torch.bfloat16, 2: torch.float16, 3: torch.float8_e4m3fn, 4: torch.int8}
+    tmap = {1: torch.bfloat16, 2: torch.float16, 3: torch.float8_e4m3fn, 4: torch.int8,
+            5: torch.float32}
     t = dev(w.view(np.uint8)).view(tmap[dtype]).view(w.shape)
     cfg = ep.LatticeRANSConfig(target_bpp=target_bpp, tile_fields=tile_fields,
                                force_scale=force_scale)
