@@ -68,7 +68,10 @@ def lib():
             "or_alpha": (C.c_float, [dbl, i64]),
             "or_encode_tiles": (i32, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, i64]),
             "or_decode_tiles": (i32, [P, P, P, i64, i32, i32, i32, P, P, P, i64, i64, P, P]),
-            "or_compress": (i32, [i32, P, i64, i64, dbl, i32, dbl, P, i64, P, P]),
+            "or_compress": (i32, [i32, P, i64, i64, dbl, i32, dbl, i32, P, i64, P, P]),
+            "or_rate_costs": (None, [P]),
+            "or_row_rates": (None, [P, P, i64, i64, P, P, P, P, P]),
+            "or_refine_select": (dbl, [P, P, i64, i32, i64, P]),
             "or_compress_bound": (i32, [i64, i64, i32, P]),
             "or_decompress": (i32, [P, i64, i64, i64, P, P, P]),
             "or_blob_fields": (i32, [P, i64, P, P, P, P, P, P, P, P]),
@@ -238,8 +241,9 @@ def decode_tiles(woff, states, words, nv, tile_fields, lanes, precision, lo, n, 
 
 
 def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
-             force_s: float = 0.0):
-    """Returns (status, blob bytes as uint8 array, s)."""
+             force_s: float = 0.0, refine: int = 0):
+    """Returns (status, blob bytes as uint8 array, s).  refine: 0, or the odd number (<= 9) of
+    candidate resolutions per row of the rate-distortion refinement."""
     w = np.ascontiguousarray(w)
     R, Cc = w.shape
     bound = C.c_int64()
@@ -250,7 +254,7 @@ def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
     nbytes = C.c_int64()
     s = C.c_double()
     st = lib().or_compress(dtype, _p(w), R, Cc, float(target_bpp), tile_fields, float(force_s),
-                           _p(blob), blob.size, C.byref(nbytes), C.byref(s))
+                           int(refine), _p(blob), blob.size, C.byref(nbytes), C.byref(s))
     if st:
         return st, None, s.value
     return st, blob[: nbytes.value].copy(), s.value
@@ -291,3 +295,32 @@ def search_scale(w, dtype, tile_fields, target_bpp, sumsq=None):
     ss = row_sumsq(w, dtype) if sumsq is None else sumsq
     return lib().or_search_scale(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
                                  target_bpp)
+
+
+def rate_costs() -> np.ndarray:
+    """Fixed-point code lengths (2^-16 bit) of frequencies 1..2^P; entry 0: a value absent from
+    the model."""
+    c = np.empty((1 << 12) + 1, np.uint32)
+    lib().or_rate_costs(_p(c))
+    return c
+
+
+def row_rates(cos, fld, rows, cols, lo, n, freq, cost) -> np.ndarray:
+    out = np.empty(rows, np.int64)
+    lib().or_row_rates(_p(np.ascontiguousarray(cos, np.uint8)),
+                       _p(np.ascontiguousarray(fld, np.int16)), rows, cols,
+                       _p(np.ascontiguousarray(lo, np.int32)),
+                       _p(np.ascontiguousarray(n, np.uint32)),
+                       _p(np.ascontiguousarray(freq, np.uint16)),
+                       _p(np.ascontiguousarray(cost, np.uint32)), _p(out))
+    return out
+
+
+def refine_select(D: np.ndarray, Rq: np.ndarray, budget_q: int):
+    """Lagrangian selection over candidates: D, Rq are [rows, nc].  Returns (lambda, sel)."""
+    D = np.ascontiguousarray(D, np.float64)
+    Rq = np.ascontiguousarray(Rq, np.int64)
+    rows, nc = D.shape
+    sel = np.empty(rows, np.int32)
+    lam = lib().or_refine_select(_p(D), _p(Rq), rows, nc, int(budget_q), _p(sel))
+    return lam, sel

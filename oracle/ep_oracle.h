@@ -78,8 +78,8 @@ int or_decode_tiles(const uint32_t* word_off, const uint32_t* states, const uint
 
 /* blob */
 int or_compress(int dt, const void* w, int64_t rows, int64_t cols, double target_bpp,
-                int tile_fields, double force_s, uint8_t* blob, int64_t cap, int64_t* out_bytes,
-                double* s_out);
+                int tile_fields, double force_s, int refine, uint8_t* blob, int64_t cap,
+                int64_t* out_bytes, double* s_out);
 int or_compress_bound(int64_t rows, int64_t cols, int tile_fields, int64_t* bytes);
 int or_decompress(const uint8_t* blob, int64_t bytes, int64_t t0, int64_t t1, void* out,
                   uint8_t* coset_out, int16_t* fields_out);
@@ -90,5 +90,13 @@ double or_estimate_bpp(int dt, const void* w, int64_t rows, int64_t cols, const 
                        int tile_fields, double s);
 double or_search_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
                        int tile_fields, double target_bpp);
+
+/* per-row rate-distortion refinement (refine = number of candidate resolutions, odd, <= 9) */
+void or_rate_costs(uint32_t* cost /* [2^P + 1]: [0] = a value absent from the model */);
+void or_row_rates(const uint8_t* cs, const int16_t* fs, int64_t rows, int64_t cols,
+                  const int32_t* lo, const uint32_t* n, const uint16_t* freq,
+                  const uint32_t* cost, int64_t* rate);
+double or_refine_select(const double* D, const int64_t* Rq, int64_t rows, int nc,
+                        int64_t budget_q, int32_t* sel);
 
 #endif
