@@ -255,6 +255,55 @@ extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64
   return finish_estimate(bits, n, rows, cols, n_sample_rows, tile_fields);
 }
 
+extern "C" void ep_rate_costs(uint32_t* h_cost) {
+  if (!h_cost) return;
+  h_cost[0] = (uint32_t)(EP_PRECISION + 1) * 65536u;
+  for (uint32_t f = 1; f <= kM; f++)
+    h_cost[f] = (uint32_t)std::llround(((double)EP_PRECISION - std::log2((double)f)) * 65536.0);
+}
+
+namespace {
+// Total rate of the per-row choice minimising D + lambda * bits (first minimum in candidate
+// order; candidates with D = +inf are not offered); the choice goes to sel.
+int64_t pick_at(const double* D, const int64_t* Rq, int64_t rows, int nc, double lambda,
+                int32_t* sel) {
+  int64_t total = 0;
+  for (int64_t r = 0; r < rows; r++) {
+    int best = -1;
+    double bj = 0.0;
+    for (int k = 0; k < nc; k++) {
+      const double d = D[r * nc + k];
+      if (std::isinf(d)) continue;
+      const double bits = (double)Rq[r * nc + k] / 65536.0;
+      const double j = d + lambda * bits;
+      if (best < 0 || j < bj) {
+        best = k;
+        bj = j;
+      }
+    }
+    if (best < 0) best = 0;
+    sel[r] = best;
+    total += Rq[r * nc + best];
+  }
+  return total;
+}
+}  // namespace
+
+extern "C" double ep_refine_select(const double* h_D, const int64_t* h_Rq, int64_t rows,
+                                   int32_t nc, int64_t budget_q, int32_t* h_sel) {
+  if (!h_D || !h_Rq || !h_sel || rows < 1 || nc < 1) return NAN;
+  if (pick_at(h_D, h_Rq, rows, nc, 0.0, h_sel) <= budget_q) return 0.0;
+  if (pick_at(h_D, h_Rq, rows, nc, std::exp2(60.0), h_sel) > budget_q) return std::exp2(60.0);
+  double lo = -60.0, hi = 60.0;
+  for (int it = 0; it < 60; it++) {
+    const double mid = 0.5 * (lo + hi);
+    if (pick_at(h_D, h_Rq, rows, nc, std::exp2(mid), h_sel) <= budget_q) hi = mid;
+    else lo = mid;
+  }
+  pick_at(h_D, h_Rq, rows, nc, std::exp2(hi), h_sel);
+  return std::exp2(hi);
+}
+
 extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fields,
                                      int64_t n_vectors, uint32_t tile_fields,
                                      const ep_tables* tables, uint32_t* h_word_off,
@@ -332,6 +381,8 @@ struct Workspace {
   size_t enc_bytes;
   uint32_t* word_off;   // encoder outputs: u32[tiles + 1], u32[1], u32[tiles * 64], u16[9 NV + 1]
   uint32_t* max_words;
+  uint32_t* cost;       // refinement: fixed-point code lengths, u32[2^P + 1]
+  int64_t* rates;       // refinement: per-row rates, i64[rows]
   uint32_t* states;
   uint16_t* words;
   size_t total;
@@ -366,6 +417,8 @@ Workspace carve(void* base, int64_t rows, int64_t cols) {
   w.max_words = reinterpret_cast<uint32_t*>(p + o); o += up(4);
   w.states = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)kK * max_tiles);
   w.words = reinterpret_cast<uint16_t*>(p + o); o += up(2 * (9 * (size_t)nv + 1));
+  w.cost = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)(kM + 1));
+  w.rates = reinterpret_cast<int64_t*>(p + o); o += up(8 * (size_t)rows);
   w.total = o;
   return w;
 }
@@ -486,7 +539,11 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
   const uint32_t F = cfg->tile_fields;
   if (F < 512 || F % 512) return EP_ERR_ARG;
-  if (cfg->refine) return EP_ERR_ARG;
+  const int nc = (int)cfg->refine;
+  if (cfg->refine > 9 || (nc > 0 && nc % 2 == 0)) return EP_ERR_ARG;
+  if (nc > 0 && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
+                  cfg->target_bpp <= 11.0))
+    return EP_ERR_ARG;
   const bool forced = cfg->force_scale > 0.0;
   if (!forced && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
                    cfg->target_bpp <= 11.0))
@@ -524,6 +581,14 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
     return ep_quantize_e8(d_w, dtype, rows, cols, ws.gains, d_sel, nsel, ws.coset, ws.fields,
                           ws.hist, ws.err, stream);
+  };
+
+  // enqueue the quantisation of all rows with the given per-row gains (histogram optional)
+  auto quantise_with = [&](const float* g, bool with_hist) -> ep_status {
+    hip(hipMemcpyAsync(ws.gains, g, 4 * rows, hipMemcpyHostToDevice, s));
+    hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
+    return ep_quantize_e8(d_w, dtype, rows, cols, ws.gains, nullptr, rows, ws.coset, ws.fields,
+                          with_hist ? ws.hist : nullptr, ws.err, stream);
   };
 
   // 2. rate search on sampled rows: per candidate the device quantises the sample, builds the
@@ -576,14 +641,90 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   }
   if (scale_out) *scale_out = sc;
 
+  // 2b. optional per-row rate-distortion refinement: the per-row gains of the chosen resolutions
+  std::vector<float> final_gains(rows);
+  for (int64_t r = 0; r < rows; r++) final_gains[r] = row_gain(sumsq[r], cols, sc);
+  if (nc > 0) {
+    const int c = (nc - 1) / 2;
+    const int64_t V = F / 8, tiles = (nv + V - 1) / V;
+    std::vector<float> gk((size_t)rows * nc), gcol(rows);
+    for (int k = 0; k < nc; k++) {
+      const double sk = sc * std::exp2((double)(k - c) / 4.0);
+      for (int64_t r = 0; r < rows; r++) gk[(size_t)r * nc + k] = row_gain(sumsq[r], cols, sk);
+    }
+    std::vector<uint32_t> cost(kM + 1);
+    ep_rate_costs(cost.data());
+    hip(hipMemcpyAsync(ws.cost, cost.data(), 4 * (size_t)(kM + 1), hipMemcpyHostToDevice, s));
+    // distortions of every candidate (model-free): the rows' LS residuals
+    std::vector<double> D((size_t)rows * nc), num(rows);
+    std::vector<int64_t> Rq((size_t)rows * nc, 0), den4(rows), rate(rows);
+    std::vector<int> offered(nc);
+    for (int k = 0; k < nc; k++) {
+      for (int64_t r = 0; r < rows; r++) gcol[r] = gk[(size_t)r * nc + k];
+      if ((st = quantise_with(gcol.data(), false)) != EP_OK) return st;
+      if ((st = ep_row_lsq(d_w, dtype, rows, cols, ws.coset, ws.fields, ws.num, ws.den4,
+                           stream)) != EP_OK)
+        return st;
+      hip(hipMemcpyAsync(num.data(), ws.num, 8 * rows, hipMemcpyDeviceToHost, s));
+      hip(hipMemcpyAsync(den4.data(), ws.den4, 8 * rows, hipMemcpyDeviceToHost, s));
+      hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+      hip(hipStreamSynchronize(s));
+      if (!hip.ok()) return EP_ERR_HIP;
+      offered[k] = err_host == 0;
+      if (!offered[k] && k == c) return (err_host & (1u << EP_ERR_RANGE)) ? EP_ERR_RANGE : EP_ERR_ARG;
+      for (int64_t r = 0; r < rows; r++) {
+        double d = INFINITY;
+        if (offered[k]) {
+          d = sumsq[r];
+          if (den4[r] != 0) d = sumsq[r] - num[r] * num[r] / ((double)den4[r] / 4.0);
+        }
+        D[(size_t)r * nc + k] = d;
+      }
+    }
+    std::vector<int32_t> sel(rows, c), next(rows);
+    ep_tables* d_T = const_cast<ep_tables*>(ep::estimate_tables(ws.rate));
+    for (int round = 0; round < 3; round++) {
+      // the model of the current selection
+      for (int64_t r = 0; r < rows; r++) gcol[r] = gk[(size_t)r * nc + sel[r]];
+      if ((st = quantise_with(gcol.data(), true)) != EP_OK) return st;
+      if ((st = ep_build_tables_gpu(ws.hist, d_T, ws.err, stream)) != EP_OK) return st;
+      uint32_t n_tab[EP_NTABLES];
+      hip(hipMemcpyAsync(n_tab, d_T->n, 4 * EP_NTABLES, hipMemcpyDeviceToHost, s));
+      hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+      hip(hipStreamSynchronize(s));
+      if (!hip.ok()) return EP_ERR_HIP;
+      if (err_host & (1u << EP_ERR_RANGE)) return EP_ERR_RANGE;
+      if (err_host & ~(1u << EP_ERR_ALPHABET)) return EP_ERR_ARG;
+      if (err_host) break;                            // the model cannot be built: stop here
+      const double budget = cfg->target_bpp * (double)rows * (double)cols -
+                            8.0 * (double)layout(rows, tiles, tables_bytes(n_tab), 0).words;
+      const int64_t budget_q = budget > 0.0 ? std::llround(budget * 65536.0) : 0;
+      // the rates of every offered candidate under this model
+      for (int k = 0; k < nc; k++) {
+        if (!offered[k]) continue;
+        for (int64_t r = 0; r < rows; r++) gcol[r] = gk[(size_t)r * nc + k];
+        if ((st = quantise_with(gcol.data(), false)) != EP_OK) return st;
+        if ((st = ep_row_rates(ws.coset, ws.fields, rows, cols, d_T, ws.cost, ws.rates,
+                               stream)) != EP_OK)
+          return st;
+        hip(hipMemcpyAsync(rate.data(), ws.rates, 8 * rows, hipMemcpyDeviceToHost, s));
+        hip(hipStreamSynchronize(s));
+        if (!hip.ok()) return EP_ERR_HIP;
+        for (int64_t r = 0; r < rows; r++) Rq[(size_t)r * nc + k] = rate[r];
+      }
+      ep_refine_select(D.data(), Rq.data(), rows, nc, budget_q, next.data());
+      sel = next;
+    }
+    for (int64_t r = 0; r < rows; r++) final_gains[r] = gk[(size_t)r * nc + sel[r]];
+  }
+
   // 3. full quantisation + histogram, 4. row least-squares scales, 5. tables (device)
   std::vector<double> num(rows);
   std::vector<int64_t> den4(rows);
   std::vector<ep_tables> tabv(1);
   ep_tables& T = tabv[0];
   {
-    const std::vector<int64_t> none;
-    const ep_status q = quantise(sc, nullptr, rows, none);
+    const ep_status q = quantise_with(final_gains.data(), true);
     if (q != EP_OK) return q == EP_ERR_HIP ? EP_ERR_HIP : EP_ERR_ARG;
     if ((st = ep_row_lsq(d_w, dtype, rows, cols, ws.coset, ws.fields, ws.num, ws.den4, stream)) !=
         EP_OK)

@@ -178,6 +178,62 @@ __global__ __launch_bounds__(64) void k_sum_bits(const uint32_t* __restrict__ hi
   if (lane == 0) *bits = acc;
 }
 
+// Rate of row blockIdx.x in units of 2^-16 bit under the device tables: the sum over its vectors
+// of cost[f] for the coset symbol (table 0) and the eight fields (tables 1 + 8c + k), where f is
+// the value's frequency, or 0 (cost[0]) for a value outside its table.  One workgroup per row;
+// the integer sum is exact, so the order of the additions does not matter.
+constexpr int kRT = 256;
+
+__global__ __launch_bounds__(kRT) void k_row_rates(const uint8_t* __restrict__ coset,
+                                                   const int16_t* __restrict__ fields,
+                                                   uint32_t vpr, const ep_tables* __restrict__ tab,
+                                                   const uint32_t* __restrict__ cost,
+                                                   int64_t* __restrict__ rate) {
+  __shared__ int32_t s_lo[EP_NTABLES];
+  __shared__ uint32_t s_n[EP_NTABLES];
+  __shared__ uint64_t s_sum[kRT / 64];
+  if (threadIdx.x < EP_NTABLES) {
+    s_lo[threadIdx.x] = tab->lo[threadIdx.x];
+    s_n[threadIdx.x] = tab->n[threadIdx.x];
+  }
+  __syncthreads();
+  auto cost_of = [&](int t, int32_t value) -> uint64_t {
+    const uint32_t i = (uint32_t)(value - s_lo[t]);
+    const uint32_t f = i < s_n[t] ? tab->freq[(size_t)t * EP_HIST_BINS + i] : 0u;
+    return cost[f];
+  };
+  const int64_t v0 = (int64_t)blockIdx.x * vpr;
+  const uint4* fv = reinterpret_cast<const uint4*>(fields);
+  uint64_t acc = 0;
+  for (uint32_t m = threadIdx.x; m < vpr; m += kRT) {
+    const uint32_t c = coset[v0 + m];
+    acc += cost_of(0, (int32_t)c);
+    const uint4 q = fv[v0 + m];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    const int tb = 1 + 8 * (int)(c & 1u);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t h = w[k >> 1];
+      const int32_t value = (k & 1) ? (int32_t)h >> 16 : (int32_t)(int16_t)(h & 0xFFFFu);
+      acc += cost_of(tb + k, value);
+    }
+  }
+  // wavefront sum, then the workgroup's
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)acc, d);
+    const uint32_t hi = __shfl_xor((uint32_t)(acc >> 32), d);
+    acc += ((uint64_t)hi << 32) | lo;
+  }
+  if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t t = 0;
+    for (int i = 0; i < kRT / 64; i++) t += s_sum[i];
+    rate[blockIdx.x] = (int64_t)t;
+  }
+}
+
 // P - log2(f) for f = 1 .. 2^P (entry 0 unused), with the host's log2.
 static const std::array<double, kNormM + 1>& cost_table() {
   static const std::array<double, kNormM + 1> tab = [] {
@@ -225,6 +281,20 @@ extern "C" ep_status ep_build_tables_gpu(const ep_hist* d_hist, ep_tables* d_out
 }
 
 extern "C" size_t ep_estimate_workspace_bytes(void) { return rate_carve(nullptr).total; }
+
+extern "C" ep_status ep_row_rates(const uint8_t* d_coset, const int16_t* d_fields, int64_t rows,
+                                  int64_t cols, const ep_tables* d_tables, const uint32_t* d_cost,
+                                  int64_t* d_rates, void* stream) {
+  if (!d_coset || !d_fields || !d_tables || !d_cost || !d_rates) return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
+  if (rows < 1 || cols < 8 || cols % 8 || rows >= ((int64_t)1 << 31) ||
+      rows * (cols / 8) >= ((int64_t)1 << 31))
+    return EP_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  k_row_rates<<<(unsigned)rows, kRT, 0, s>>>(d_coset, d_fields, (uint32_t)(cols / 8), d_tables,
+                                             d_cost, d_rates);
+  return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
 
 // Internal: the device part of the estimate, enqueued on `s`; the sum of bits lands in
 // h_bits and the table sizes in h_n after the stream synchronises.  Returns false on a HIP error.

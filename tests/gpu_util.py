@@ -123,7 +123,7 @@ class GpuBlob:
 
 
 def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
-                 force_scale: float = 0.0):
+                 force_scale: float = 0.0, refine: int = 0):
     """Library compress of a device copy of w -> (blob bytes, s)."""
     import torch
 
@@ -132,7 +132,7 @@ def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
             5: torch.float32}
     t = dev(w.view(np.uint8)).view(tmap[dtype]).view(w.shape)
     cfg = ep.LatticeRANSConfig(target_bpp=target_bpp, tile_fields=tile_fields,
-                               force_scale=force_scale)
+                               force_scale=force_scale, refine=refine)
     c = ep.compress(t, cfg)
     return c.blob, c.scale
 

@@ -185,3 +185,24 @@ def test_encode_workspace_bytes(ep):
         assert ep.ep_encode_workspace_bytes(nv, F) == want
     assert ep.ep_encode_workspace_bytes(0, 4096) == 0
     assert ep.ep_encode_workspace_bytes(100, 1000) == 0
+
+
+def test_rate_costs_match_oracle(ep, orc):
+    assert np.array_equal(ep.ep_rate_costs(), orc.rate_costs())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_refine_select_matches_oracle(ep, orc, seed):
+    g = np.random.Generator(np.random.PCG64(900 + seed))
+    rows, nc = int(g.integers(1, 300)), [1, 3, 5, 9, 3, 5][seed]
+    Rq = g.integers(0, 1 << 30, (rows, nc)).astype(np.int64)
+    D = g.uniform(0.0, 5.0, (rows, nc))
+    if nc > 1:
+        D[g.random((rows, nc)) < 0.1] = np.inf          # candidates not offered
+        D[:, (nc - 1) // 2] = g.uniform(0.0, 5.0, rows)  # the middle one always is
+    lo, hi = int(Rq.min(axis=1).sum()), int(Rq.max(axis=1).sum())
+    for budget in (lo - 1, lo, (lo + hi) // 2, hi, hi + 1, 0):
+        lam, sel = ep.ep_refine_select(D, Rq, budget)
+        lam_o, sel_o = orc.refine_select(D, Rq, budget)
+        assert np.float64(lam).view(np.uint64) == np.float64(lam_o).view(np.uint64)
+        assert np.array_equal(sel, sel_o)
