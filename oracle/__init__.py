@@ -169,7 +169,7 @@ def quantize(w: np.ndarray, dtype: int, gains_: np.ndarray, row_sel=None):
         sel_p = _p(sel)
     else:
         nsel, sel_p = R, None
-    nv = nsel * (Cc // 8)
+    nv = nsel * ((Cc + 7) // 8)
     cos = np.empty(nv, np.uint8)
     fld = np.empty(nv * 8, np.int16)
     st = lib().or_quantize(dtype, _p(w), R, Cc, _p(g), sel_p, nsel, _p(cos), _p(fld))
@@ -276,7 +276,7 @@ def decompress(blob: np.ndarray, t0: int = 0, t1: int = -1, want_fields: bool = 
     info = blob_fields(blob)
     R, Cc, dt = info["rows"], info["cols"], info["dtype"]
     out = np.zeros((R, Cc), bits_dtype(dt))
-    nv = R * Cc // 8
+    nv = R * ((Cc + 7) // 8)
     cos = np.zeros(nv, np.uint8) if want_fields else None
     fld = np.zeros(nv * 8, np.int16) if want_fields else None
     st = lib().or_decompress(_p(blob), blob.size, t0, t1, _p(out),
