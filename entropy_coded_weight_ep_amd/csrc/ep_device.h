@@ -63,6 +63,39 @@ __device__ __forceinline__ typename RawVec<DT>::T raw_load(const void* base, int
   return reinterpret_cast<const typename RawVec<DT>::T*>(base)[vec];
 }
 
+// One container element's bits.
+template <int DT>
+__device__ __forceinline__ uint32_t elem_bits(const void* base, int64_t i) {
+  if constexpr (DT == EP_FP32) return static_cast<const uint32_t*>(base)[i];
+  else if constexpr (DT == EP_BF16 || DT == EP_FP16) return static_cast<const uint16_t*>(base)[i];
+  else return static_cast<const uint8_t*>(base)[i];
+}
+
+// Vector m of a row of `cols` elements starting at element e0, for a width that is not a multiple
+// of 8: element loads, and zeros for the coordinates past the row's end.
+template <int DT>
+__device__ __forceinline__ typename RawVec<DT>::T raw_load_padded(const void* base, int64_t e0,
+                                                                  int64_t m, int64_t cols) {
+  uint32_t b[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int64_t c = 8 * m + k;
+    b[k] = c < cols ? elem_bits<DT>(base, e0 + c) : 0u;
+  }
+  typename RawVec<DT>::T q;
+  if constexpr (DT == EP_FP32) {
+    q.a = make_uint4(b[0], b[1], b[2], b[3]);
+    q.b = make_uint4(b[4], b[5], b[6], b[7]);
+  } else if constexpr (DT == EP_BF16 || DT == EP_FP16) {
+    q = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                   b[6] | (b[7] << 16));
+  } else {
+    q = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                   b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  }
+  return q;
+}
+
 template <int DT>
 __device__ __forceinline__ typename RawVec<DT>::T raw_zero() {
   typename RawVec<DT>::T z;

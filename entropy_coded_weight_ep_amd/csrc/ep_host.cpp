@@ -214,7 +214,7 @@ namespace {
 double finish_estimate(double acc, const uint32_t* n, int64_t rows, int64_t cols,
                        int64_t n_sample_rows, uint32_t tile_fields) {
   const double bits = acc * ((double)rows / (double)n_sample_rows);
-  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
+  const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
   const Layout L = layout(rows, tiles, tables_bytes(n), 0);
   const double meta = (double)L.words;      // everything before the payload words
   return (bits + 8.0 * meta) / ((double)rows * (double)cols);
@@ -223,7 +223,7 @@ double finish_estimate(double acc, const uint32_t* n, int64_t rows, int64_t cols
 
 extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t cols,
                                   int64_t n_sample_rows, uint32_t tile_fields) {
-  if (!h_hist || rows < 1 || cols < 8 || n_sample_rows < 1 || tile_fields < 8) return INFINITY;
+  if (!h_hist || rows < 1 || cols < 1 || n_sample_rows < 1 || tile_fields < 8) return INFINITY;
   std::vector<ep_tables> tv(1);
   ep_tables& T = tv[0];
   if (ep_build_tables(h_hist, EP_PRECISION, &T) != EP_OK) return INFINITY;
@@ -242,7 +242,7 @@ extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t c
 extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64_t cols,
                                       int64_t n_sample_rows, uint32_t tile_fields,
                                       void* d_workspace, size_t workspace_bytes, void* stream) {
-  if (!d_hist || !d_workspace || rows < 1 || cols < 8 || n_sample_rows < 1 || tile_fields < 8)
+  if (!d_hist || !d_workspace || rows < 1 || cols < 1 || n_sample_rows < 1 || tile_fields < 8)
     return INFINITY;
   if (workspace_bytes < ep_estimate_workspace_bytes()) return INFINITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -356,9 +356,9 @@ extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fi
 extern "C" ep_status ep_compress_bound(int64_t rows, int64_t cols, uint32_t tile_fields,
                                        size_t* bytes) {
   if (!bytes) return EP_ERR_ARG;
-  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   if (tile_fields < 512 || tile_fields % 512) return EP_ERR_ARG;
-  const int64_t nv = rows * (cols / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
+  const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
   uint32_t nmax[EP_NTABLES];
   for (int t = 0; t < EP_NTABLES; t++) nmax[t] = 65535;
   *bytes = (size_t)layout(rows, tiles, tables_bytes(nmax), 9 * nv).total;
@@ -396,7 +396,7 @@ Workspace carve(void* base, int64_t rows, int64_t cols) {
   uint8_t* p = static_cast<uint8_t*>(base);
   size_t o = 0;
   Workspace w;
-  const int64_t nv = rows * (cols / 8);
+  const int64_t nv = rows * ((cols + 7) / 8);
   w.hist = reinterpret_cast<ep_hist*>(p + o); o += up(sizeof(ep_hist));
   w.sumsq = reinterpret_cast<double*>(p + o); o += up(8 * rows);
   w.gains = reinterpret_cast<float*>(p + o); o += up(4 * rows);
@@ -431,7 +431,7 @@ inline float row_gain(double sumsq, int64_t cols, double s) {
 }  // namespace
 
 extern "C" size_t ep_compress_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 8) return 0;
+  if (rows < 1 || cols < 1) return 0;
   return carve(nullptr, rows, cols).total;
 }
 
@@ -460,10 +460,10 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   std::memcpy(&I.max_tile_words, b + 56, 4);
   if (I.dtype < EP_BF16 || I.dtype > EP_FP32) return EP_ERR_DTYPE;
   if (I.precision != EP_PRECISION || I.lanes != EP_LANES) return EP_ERR_VERSION;
-  if (I.rows < 1 || I.cols < 8 || I.cols % 8 || I.tile_fields < 512 || I.tile_fields % 512)
+  if (I.rows < 1 || I.cols < 1 || I.tile_fields < 512 || I.tile_fields % 512)
     return EP_ERR_CORRUPT;
   if (I.rows > ((int64_t)1 << 40) || I.cols > ((int64_t)1 << 40)) return EP_ERR_CORRUPT;
-  const int64_t nv = I.rows * (I.cols / 8), V = I.tile_fields / 8;
+  const int64_t nv = I.rows * ((I.cols + 7) / 8), V = I.tile_fields / 8;
   if (I.tiles != (nv + V - 1) / V) return EP_ERR_CORRUPT;
   if (I.payload_words < 0 || I.payload_words > ((int64_t)1 << 32)) return EP_ERR_CORRUPT;
   const Layout L = layout(I.rows, I.tiles, tb, I.payload_words);
@@ -536,7 +536,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
                                  void* stream) {
   if (!d_w || !cfg || !d_workspace || !h_blob || !out_bytes) return EP_ERR_ARG;
   if (dtype < EP_BF16 || dtype > EP_FP32) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   const uint32_t F = cfg->tile_fields;
   if (F < 512 || F % 512) return EP_ERR_ARG;
   const int nc = (int)cfg->refine;
@@ -548,7 +548,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   if (!forced && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
                    cfg->target_bpp <= 11.0))
     return EP_ERR_ARG;
-  const int64_t nv = rows * (cols / 8);
+  const int64_t nv = rows * ((cols + 7) / 8);
   if (nv >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
   if (workspace_bytes < ep_compress_workspace_bytes(rows, cols)) return EP_ERR_CAPACITY;
   const Workspace ws = carve(d_workspace, rows, cols);

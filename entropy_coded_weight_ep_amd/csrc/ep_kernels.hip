@@ -29,23 +29,31 @@ namespace ep {
 // ------------------------------------------------------------------------------------------
 constexpr int kRowChunk = 8;                       // vectors per lane per prefetch stage
 
-template <int DT>
+// PAD: a width that is not a multiple of 8; the zeros past the row's end add exactly nothing.
+template <int DT, bool PAD>
+__device__ __forceinline__ typename RawVec<DT>::T row_vec(const void* w, int64_t r, int64_t cols,
+                                                          int64_t vpr, int64_t m) {
+  if constexpr (PAD) return raw_load_padded<DT>(w, r * cols, m, cols);
+  else return raw_load<DT>(w, r * vpr + m);
+}
+
+template <int DT, bool PAD>
 __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, int64_t rows,
                                                   int64_t cols, double* __restrict__ out) {
   using Raw = typename RawVec<DT>::T;
   const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (r >= rows) return;
-  const int64_t vpr = cols / 8, v_row = r * vpr;
+  const int64_t vpr = (cols + 7) / 8;
   Raw cur[kRowChunk], nxt[kRowChunk];
 #pragma unroll
   for (int k = 0; k < kRowChunk; k++)
-    if (k < vpr) cur[k] = raw_load<DT>(w, v_row + k);
+    if (k < vpr) cur[k] = row_vec<DT, PAD>(w, r, cols, vpr, k);
   double acc = 0.0;
   for (int64_t v0 = 0; v0 < vpr; v0 += kRowChunk) {
     const int64_t v1 = v0 + kRowChunk;
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++)
-      if (v1 + k < vpr) nxt[k] = raw_load<DT>(w, v_row + v1 + k);
+      if (v1 + k < vpr) nxt[k] = row_vec<DT, PAD>(w, r, cols, vpr, v1 + k);
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++) {
       if (v0 + k < vpr) {
@@ -144,7 +152,7 @@ struct QIn {
   bool ok;
 };
 
-template <int DT>
+template <int DT, bool PAD>
 __device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t rows,
                                            int64_t cols, const float* __restrict__ gain,
                                            const int64_t* __restrict__ row_index, uint32_t v,
@@ -160,7 +168,7 @@ __device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t r
   q.raw = raw_zero<DT>();
   q.g = 0.0f;
   if (q.ok) {
-    q.raw = raw_load<DT>(w, r * (cols / 8) + (int64_t)m);
+    q.raw = row_vec<DT, PAD>(w, r, cols, vpr, (int64_t)m);
     q.g = gain[r];
   }
   return q;
@@ -175,7 +183,7 @@ __device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t r
 // once.
 constexpr int kQThreads = 1024;
 
-template <int DT>
+template <int DT, bool PAD>
 __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
     const void* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ gain,
     const int64_t* __restrict__ row_index, uint32_t n_vec, uint32_t vpr, double inv_vpr,
@@ -192,11 +200,11 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
   const uint32_t stride = gridDim.x * (uint32_t)kQThreads;
   uint32_t v = blockIdx.x * (uint32_t)kQThreads + threadIdx.x;
   QIn<DT> cur;
-  if (v < n_vec) cur = q_fetch<DT>(w, rows, cols, gain, row_index, v, vpr, inv_vpr);
+  if (v < n_vec) cur = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, v, vpr, inv_vpr);
   for (; v < n_vec; v += stride) {
     QIn<DT> nxt;
     const bool more = v + stride < n_vec;         // (no overflow: n_vec + stride < 2^32)
-    if (more) nxt = q_fetch<DT>(w, rows, cols, gain, row_index, v + stride, vpr, inv_vpr);
+    if (more) nxt = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, v + stride, vpr, inv_vpr);
     if (!cur.ok) {                                // a row index outside the tensor: skip, report
       bad_row = true;
     } else {
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
 // cosets of the next kRowChunk vectors loaded while the current ones are summed).
 // num = sum w * p (fp64, left to right; each product exact), den4 = sum (2p)^2 (int64).
 // ------------------------------------------------------------------------------------------
-template <int DT>
+template <int DT, bool PAD>
 __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int64_t rows,
                                                 int64_t cols, const uint8_t* __restrict__ coset,
                                                 const int16_t* __restrict__ fields,
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
   using Raw = typename RawVec<DT>::T;
   const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (r >= rows) return;
-  const int64_t vpr = cols / 8, v_row = r * vpr;
+  const int64_t vpr = (cols + 7) / 8, v_row = r * vpr;
   const uint4* fv = reinterpret_cast<const uint4*>(fields);
   Raw cw[kRowChunk], nw[kRowChunk];
   uint4 cf[kRowChunk], nf[kRowChunk];
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 #pragma unroll
   for (int k = 0; k < kRowChunk; k++) {
     if (k < vpr) {
-      cw[k] = raw_load<DT>(w, v_row + k);
+      cw[k] = row_vec<DT, PAD>(w, r, cols, vpr, k);
       cf[k] = fv[v_row + k];
       cc[k] = coset[v_row + k];
     }
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++) {
       if (v1 + k < vpr) {
-        nw[k] = raw_load<DT>(w, v_row + v1 + k);
+        nw[k] = row_vec<DT, PAD>(w, r, cols, vpr, v1 + k);
         nf[k] = fv[v_row + v1 + k];
         nc[k] = coset[v_row + v1 + k];
       }
@@ -336,6 +344,7 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
         const int32_t c = (int32_t)cc[k];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
+          if (PAD && 8 * (v0 + k) + i >= cols) break;     // padding: not a weight
           const int64_t h = 2 * (int64_t)f[i] + c;
           const double p = (double)h * 0.5;
           acc = __dadd_rn(acc, __dmul_rn((double)x[i], p));
@@ -413,16 +422,21 @@ extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, 
   if (!d_w || !d_out) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_w) & 15u) return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + 63) / 64));
+  const bool pad = cols % 8 != 0;
+#define EP_S(DT)                                                                              \
+  (pad ? k_row_sumsq<DT, true><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out)                    \
+       : k_row_sumsq<DT, false><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out))
   switch (dtype) {
-    case EP_BF16: k_row_sumsq<EP_BF16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
-    case EP_FP16: k_row_sumsq<EP_FP16><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
-    case EP_FP8_E4M3FN: k_row_sumsq<EP_FP8_E4M3FN><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
-    case EP_FP32: k_row_sumsq<EP_FP32><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
-    default: k_row_sumsq<EP_INT8><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out); break;
+    case EP_BF16: EP_S(EP_BF16); break;
+    case EP_FP16: EP_S(EP_FP16); break;
+    case EP_FP8_E4M3FN: EP_S(EP_FP8_E4M3FN); break;
+    case EP_FP32: EP_S(EP_FP32); break;
+    default: EP_S(EP_INT8); break;
   }
+#undef EP_S
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -434,10 +448,10 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   const int64_t nsel = d_row_index ? n_rows_sel : rows;
   if (nsel < 0 || (d_row_index && nsel > (int64_t)1 << 31)) return EP_ERR_ARG;
-  const int64_t nvec = nsel * (cols / 8);
+  const int64_t nvec = nsel * ((cols + 7) / 8);
   if (nvec >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hist = d_hist ? d_hist->counts : nullptr;
@@ -450,11 +464,14 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
   int64_t blocks = (nvec + kQThreads - 1) / kQThreads;
   if (blocks > 2 * kCUs) blocks = 2 * kCUs;
   const dim3 grid((unsigned)blocks);
-  const uint32_t nv = (uint32_t)nvec, vpr = (uint32_t)(cols / 8);
+  const uint32_t nv = (uint32_t)nvec, vpr = (uint32_t)((cols + 7) / 8);
+  const bool pad = cols % 8 != 0;
   const double inv_vpr = 1.0 / (double)vpr;
-#define EP_Q(DT) k_quantize_e8<DT><<<grid, kQThreads, 0, s>>>(d_w, rows, cols, d_row_gain,    \
-                                                              d_row_index, nv, vpr, inv_vpr,  \
-                                                              d_coset, d_fields, hist, d_err)
+#define EP_Q1(DT, PAD)                                                                        \
+  k_quantize_e8<DT, PAD><<<grid, kQThreads, 0, s>>>(d_w, rows, cols, d_row_gain, d_row_index, \
+                                                    nv, vpr, inv_vpr, d_coset, d_fields, hist, \
+                                                    d_err)
+#define EP_Q(DT) (pad ? EP_Q1(DT, true) : EP_Q1(DT, false))
   switch (dtype) {
     case EP_BF16: EP_Q(EP_BF16); break;
     case EP_FP16: EP_Q(EP_FP16); break;
@@ -463,6 +480,7 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
     default: EP_Q(EP_INT8); break;
   }
 #undef EP_Q
+#undef EP_Q1
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -473,10 +491,13 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 8 || cols % 8) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + 63) / 64));
-#define EP_L(DT) k_row_lsq<DT><<<grid, 64, 0, s>>>(d_w, rows, cols, d_coset, d_fields, d_num, d_den4)
+  const bool pad = cols % 8 != 0;
+#define EP_L1(DT, PAD)                                                                        \
+  k_row_lsq<DT, PAD><<<grid, 64, 0, s>>>(d_w, rows, cols, d_coset, d_fields, d_num, d_den4)
+#define EP_L(DT) (pad ? EP_L1(DT, true) : EP_L1(DT, false))
   switch (dtype) {
     case EP_BF16: EP_L(EP_BF16); break;
     case EP_FP16: EP_L(EP_FP16); break;
@@ -485,6 +506,7 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
     default: EP_L(EP_INT8); break;
   }
 #undef EP_L
+#undef EP_L1
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -529,8 +551,9 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       return EP_ERR_ARG;
     if (in.precision != EP_PRECISION || in.lanes != EP_LANES) return EP_ERR_VERSION;
     if (in.dtype != i0.dtype || in.tile_fields != i0.tile_fields) return EP_ERR_ARG;
-    if (in.rows < 1 || in.cols < 8 || in.rows * in.cols / 8 >= ((int64_t)1 << 31) ||
-        in.tiles < 1 || in.tiles != (in.rows * in.cols / 8 + J * 64 - 1) / (J * 64))
+    const int64_t nv_in = in.rows * ((in.cols + 7) / 8);
+    if (in.rows < 1 || in.cols < 1 || nv_in >= ((int64_t)1 << 31) || in.tiles < 1 ||
+        in.tiles != (nv_in + J * 64 - 1) / (J * 64))
       return EP_ERR_SHAPE;
     maxw = std::max(maxw, in.max_tile_words);
     big |= in.big_alphabet != 0;
@@ -610,7 +633,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     a.wg_begin[0] = 0;
     for (int i = 0; i < n; i++) {
       const ep_blob_info& in = infos[i];
-      const int64_t nv = in.rows * in.cols / 8;
+      const int64_t nv = in.rows * ((in.cols + 7) / 8);
       const uint32_t tiles = (uint32_t)in.tiles;
       const bool last_ragged = (uint64_t)tiles * V != (uint64_t)nv;
       const uint32_t t0 = ragged ? tiles - 1 : 0;
@@ -628,7 +651,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       b.tile_begin = t0;
       b.tile_end = t1;
       b.n_vec = (uint32_t)nv;
-      b.vpr = (uint32_t)(in.cols / 8);
+      b.vpr = (uint32_t)((in.cols + 7) / 8);
       b.max_tile_words = in.max_tile_words;
       b.coset_f0 = in.coset_freq0;
       b.lo0 = in.lo[0];

@@ -287,11 +287,11 @@ extern "C" ep_status ep_row_rates(const uint8_t* d_coset, const int16_t* d_field
                                   int64_t* d_rates, void* stream) {
   if (!d_coset || !d_fields || !d_tables || !d_cost || !d_rates) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
-  if (rows < 1 || cols < 8 || cols % 8 || rows >= ((int64_t)1 << 31) ||
-      rows * (cols / 8) >= ((int64_t)1 << 31))
+  if (rows < 1 || cols < 1 || rows >= ((int64_t)1 << 31) ||
+      rows * ((cols + 7) / 8) >= ((int64_t)1 << 31))
     return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  k_row_rates<<<(unsigned)rows, kRT, 0, s>>>(d_coset, d_fields, (uint32_t)(cols / 8), d_tables,
+  k_row_rates<<<(unsigned)rows, kRT, 0, s>>>(d_coset, d_fields, (uint32_t)((cols + 7) / 8), d_tables,
                                              d_cost, d_rates);
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }

@@ -59,7 +59,7 @@ def gpu_quantize(w: np.ndarray, dtype: int, gains: np.ndarray, row_sel=None, wit
         nsel = len(row_sel)
     else:
         d_sel, nsel = None, R
-    nv = nsel * (C // 8)
+    nv = nsel * ((C + 7) // 8)
     d_cos = torch.zeros(max(nv, 1), dtype=torch.uint8, device="cuda")
     d_fld = torch.zeros(max(nv * 8, 8), dtype=torch.int16, device="cuda")
     d_hist = torch.zeros(ep.HIST_BYTES // 4, dtype=torch.int32, device="cuda") if with_hist else None
@@ -97,9 +97,12 @@ class GpuBlob:
         self.d_tab = torch.zeros(ep.EP_DEC_TABLE_BYTES, dtype=torch.uint8, device="cuda")
         assert ep.ep_prepare_decode(self.d_blob, self.info, self.d_tab) == 0
 
+    def pitch(self):
+        return (self.info.cols + 7) // 8 * 8
+
     def out_bytes(self):
         esize = {1: 2, 2: 2, 3: 1, 4: 1, 5: 4}[self.info.dtype]
-        return self.info.rows * self.info.cols * esize
+        return self.info.rows * self.pitch() * esize
 
     def decode(self, d_out=None, flags=None):
         """Returns (err word, output container bits as numpy [rows, cols]).  flags: None for
@@ -119,7 +122,8 @@ class GpuBlob:
         out = host(d_out)
         dt = self.info.dtype
         npdt = {1: np.uint16, 2: np.uint16, 3: np.uint8, 4: np.int8, 5: np.uint32}[dt]
-        return int(host(d_err)[0]), out.view(npdt).reshape(self.info.rows, self.info.cols)
+        full = out.view(npdt).reshape(self.info.rows, self.pitch())
+        return int(host(d_err)[0]), np.ascontiguousarray(full[:, :self.info.cols])
 
 
 def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,

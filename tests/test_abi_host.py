@@ -171,8 +171,14 @@ def test_compress_bound_covers_blobs(ep, orc):
         w = S.workload_weights(key, R, Cc)
         st, blob, s = orc.compress(w, wl["dtype"], 11.0, wl["tile_fields"])
         assert blob.size <= ep.ep_compress_bound(R, Cc, wl["tile_fields"])
+    w = S.lognormal_rows(50, 1001, seed=7)              # a width that is not a multiple of 8
+    st, blob, s = orc.compress(w, S.BF16, 11.0, 4096)
+    assert st == 0 and blob.size <= ep.ep_compress_bound(50, 1001, 4096)
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0 and (info.rows, info.cols) == (50, 1001)
+    assert info.tiles == (50 * 126 + 511) // 512
     with pytest.raises(ep.EPError):
-        ep.ep_compress_bound(4, 12, 4096)
+        ep.ep_compress_bound(4, 0, 4096)
 
 
 def test_encode_workspace_bytes(ep):
