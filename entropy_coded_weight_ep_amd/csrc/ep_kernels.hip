@@ -563,11 +563,15 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // Words region per wave.  Linear: the aligned chunks of the largest tile plus one wave of
   // slack.  Ring: a power of two of at least 512 words and 2/7 of the largest tile (two field
   // phases' worth), refilled as the tile is decoded; used only when it keeps more tiles resident.
+  // Half that ring is also offered (automatic choice only): a heavy phase then waits for its
+  // refill, but when LDS is what limits the waves per CU (wide alphabets at high rates) the
+  // extra resident tiles hide more of the rANS chains' latency.
   const uint32_t lin_stride = ((maxw + 7u + 7u) & ~7u) + 64u;
   uint32_t ring_stride = 512u;
   while (layout != EP_DECODE_RING_MIN && ring_stride < 8192u &&
          (uint64_t)ring_stride * 7u < 2ull * maxw)
     ring_stride <<= 1;
+  const uint32_t ring_half = (layout == 0 && ring_stride >= 1024u) ? ring_stride / 2 : ring_stride;
   // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
   // per wave 256 B of states and the words region.  Waves per workgroup and layout: the choice
   // that keeps the most tiles resident at once; ties go to the linear layout, then to the smaller
@@ -581,28 +585,32 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   const int max_waves = J <= 16 ? kDecWaves : kDecWaves / 2;
   int waves = 0;
   bool ring = false;
+  uint32_t stride = 0;
   int64_t best = -1;
-  for (int lay = 0; lay < 2; lay++) {
-    const bool rg = lay == 1;
+  // candidates: linear (ties go to it, and among its sizes to the smaller workgroup), then the
+  // full ring and the half ring, each taken only when it keeps strictly more tiles resident
+  for (int lay = 0; lay < 3; lay++) {
+    const bool rg = lay >= 1;
     if (layout == EP_DECODE_LINEAR && rg) continue;
     if ((layout == EP_DECODE_RING || layout == EP_DECODE_RING_MIN) && !rg) continue;
-    if (rg && layout == 0 && ring_stride >= lin_stride) continue;
-    const uint32_t stride = rg ? ring_stride : lin_stride;
+    if (lay == 2 && ring_half == ring_stride) continue;
+    const uint32_t st = lay == 0 ? lin_stride : (lay == 1 ? ring_stride : ring_half);
+    if (rg && layout == 0 && st >= lin_stride) continue;
     for (int w = max_waves; w >= 1; w >>= 1) {
-      if ((int64_t)lds_of(w, stride) > kLdsPerCU) continue;
+      if ((int64_t)lds_of(w, st) > kLdsPerCU) continue;
       const int64_t per_cu =
-          std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, stride), waves_per_cu / w);
+          std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, st), waves_per_cu / w);
       const int64_t grid = (total_tiles + w - 1) / w;
       const int64_t resident = std::min(grid, kCUs * per_cu) * w;
       if (resident > best || (resident == best && !rg)) {
         best = resident;
         waves = w;
         ring = rg;
+        stride = st;
       }
     }
   }
   if (waves == 0) return EP_ERR_VERSION;             // one tile's words do not fit in LDS
-  const uint32_t stride = ring ? ring_stride : lin_stride;
   const size_t lds = lds_of(waves, stride);
   const uint32_t V = (uint32_t)i0.tile_fields / 8;
 
