@@ -580,9 +580,11 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   auto lds_of = [&](int w, uint32_t stride) {
     return lds_tables + (size_t)w * (256 + (size_t)stride * 2);
   };
-  // waves per SIMD the decoder's registers allow: 8, 4 and 2 for 8, 16 and 32 vectors per lane
-  const int64_t waves_per_cu = 4 * (J <= 8 ? 8 : (J <= 16 ? 4 : 2));
-  const int max_waves = J <= 16 ? kDecWaves : kDecWaves / 2;
+  // waves per SIMD the decoder's registers allow: 8, 4 and 4 for 8, 16 and 32 vectors per lane
+  // (2 at 32 with wide alphabets, whose fields take 16 bits each)
+  const int occ = J <= 8 ? 8 : (J <= 16 ? 4 : (big ? 2 : 4));
+  const int64_t waves_per_cu = 4 * occ;
+  const int max_waves = occ >= 4 ? kDecWaves : kDecWaves / 2;
   int waves = 0;
   bool ring = false;
   uint32_t stride = 0;
