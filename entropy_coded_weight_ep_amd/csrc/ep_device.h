@@ -19,15 +19,6 @@ constexpr uint32_t kMask = kM - 1u;
 // ------------------------------------------------------------------------------------------
 // Containers
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ float fp8e4m3_to_f32(uint32_t b) {
-  uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
-  float v;
-  if (e == 0) v = (float)m * 0.001953125f;                       // m * 2^-9, exact
-  else if (e == 15 && m == 7) v = __builtin_nanf("");
-  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));       // rebias 7 -> 127
-  return s ? -v : v;
-}
-
 template <int DT>
 __device__ __forceinline__ float widen(uint32_t bits) {
   if constexpr (DT == EP_BF16) {
@@ -36,7 +27,8 @@ __device__ __forceinline__ float widen(uint32_t bits) {
     _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits);
     return (float)h;
   } else if constexpr (DT == EP_FP8_E4M3FN) {
-    return fp8e4m3_to_f32(bits);
+    // gfx950's conversion reads the OCP E4M3FN encoding (exact; S.1111.111 is NaN)
+    return __builtin_amdgcn_cvt_f32_fp8((int)bits, 0);
   } else if constexpr (DT == EP_FP32) {
     return __uint_as_float(bits);
   } else {
@@ -116,6 +108,15 @@ __device__ __forceinline__ void raw_widen(const typename RawVec<DT>::T& q, float
       out[2 * i] = widen<DT>(w[i] & 0xFFFFu);
       out[2 * i + 1] = widen<DT>(w[i] >> 16);
     }
+  } else if constexpr (DT == EP_FP8_E4M3FN) {
+    out[0] = __builtin_amdgcn_cvt_f32_fp8((int)q.x, 0);
+    out[1] = __builtin_amdgcn_cvt_f32_fp8((int)q.x, 1);
+    out[2] = __builtin_amdgcn_cvt_f32_fp8((int)q.x, 2);
+    out[3] = __builtin_amdgcn_cvt_f32_fp8((int)q.x, 3);
+    out[4] = __builtin_amdgcn_cvt_f32_fp8((int)q.y, 0);
+    out[5] = __builtin_amdgcn_cvt_f32_fp8((int)q.y, 1);
+    out[6] = __builtin_amdgcn_cvt_f32_fp8((int)q.y, 2);
+    out[7] = __builtin_amdgcn_cvt_f32_fp8((int)q.y, 3);
   } else {
     const uint32_t w[2] = {q.x, q.y};
 #pragma unroll

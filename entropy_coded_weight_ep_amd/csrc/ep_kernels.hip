@@ -44,16 +44,17 @@ __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, in
   const int64_t r = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (r >= rows) return;
   const int64_t vpr = (cols + 7) / 8;
+  // loads past the row's end re-read its last vector (never summed): no branch around a load,
+  // so the wait before a chunk covers only that chunk's loads, not the prefetch behind it
+  auto vec = [&](int64_t m) { return row_vec<DT, PAD>(w, r, cols, vpr, m < vpr ? m : vpr - 1); };
   Raw cur[kRowChunk], nxt[kRowChunk];
 #pragma unroll
-  for (int k = 0; k < kRowChunk; k++)
-    if (k < vpr) cur[k] = row_vec<DT, PAD>(w, r, cols, vpr, k);
+  for (int k = 0; k < kRowChunk; k++) cur[k] = vec(k);
   double acc = 0.0;
   for (int64_t v0 = 0; v0 < vpr; v0 += kRowChunk) {
     const int64_t v1 = v0 + kRowChunk;
 #pragma unroll
-    for (int k = 0; k < kRowChunk; k++)
-      if (v1 + k < vpr) nxt[k] = row_vec<DT, PAD>(w, r, cols, vpr, v1 + k);
+    for (int k = 0; k < kRowChunk; k++) nxt[k] = vec(v1 + k);
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++) {
       if (v0 + k < vpr) {
@@ -137,6 +138,14 @@ __device__ __forceinline__ int e8_nearest(const float x[8], int32_t z[8]) {
 constexpr int kHistWin = 512;
 constexpr int kHistOff = 256;
 constexpr int kHistStride = 514;
+// The hottest bins: values [-16, 15] of the 16 field tables in four copies, copy = lane & 3, so
+// that at most 16 lanes of a wavefront add to the same counter (the ds_add of many lanes to one
+// address is serialised).  Tables 33 counters apart, copies 528 apart (16 banks).
+constexpr int kNarrowWin = 32;
+constexpr int kNarrowOff = 16;
+constexpr int kNarrowStride = 33;
+constexpr int kNarrowCopies = 4;
+constexpr int kNarrowBins = kNarrowCopies * 16 * kNarrowStride;
 
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -190,9 +199,11 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
     uint8_t* __restrict__ coset, int16_t* __restrict__ fields, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ err) {
   __shared__ uint32_t sh[EP_NTABLES * kHistStride];
+  __shared__ uint32_t sn[kNarrowBins];
   const bool do_hist = hist != nullptr;
   if (do_hist) {
     for (int i = threadIdx.x; i < EP_NTABLES * kHistStride; i += kQThreads) sh[i] = 0;
+    for (int i = threadIdx.x; i < kNarrowBins; i += kQThreads) sn[i] = 0;
     __syncthreads();
   }
   bool bad = false, bad_row = false;
@@ -246,10 +257,18 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
         n_c0 += 1u - (uint32_t)c;
         // bins of value 0 of this vector's coset tables (field k at + k * kHistStride)
         uint32_t* const hc = sh + (1 + 8 * c) * kHistStride + kHistOff;
-        uint32_t orr = 0;
+        uint32_t orr = 0, orn = 0;
 #pragma unroll
-        for (int k = 0; k < 8; k++) orr |= (uint32_t)(f[k] + kHistOff);
-        if (orr < (uint32_t)kHistWin) {           // every field inside the window: the usual case
+        for (int k = 0; k < 8; k++) {
+          orr |= (uint32_t)(f[k] + kHistOff);
+          orn |= (uint32_t)(f[k] + kNarrowOff);
+        }
+        if (orn < (uint32_t)kNarrowWin) {         // every field among the hottest values
+          uint32_t* const hn =
+              sn + ((threadIdx.x & (kNarrowCopies - 1)) * 16 + 8 * c) * kNarrowStride + kNarrowOff;
+#pragma unroll
+          for (int k = 0; k < 8; k++) atomicAdd(&hn[k * kNarrowStride + f[k]], 1u);
+        } else if (orr < (uint32_t)kHistWin) {    // every field inside the window
 #pragma unroll
           for (int k = 0; k < 8; k++) atomicAdd(&hc[k * kHistStride + f[k]], 1u);
         } else {
@@ -271,6 +290,15 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
   if (do_hist) {
     if (n_c0) atomicAdd(&sh[kHistOff + 0], n_c0);
     if (n_c1) atomicAdd(&sh[kHistOff + 1], n_c1);
+    __syncthreads();
+    // fold the copies of the hottest bins into the window (one thread per bin)
+    for (int i = threadIdx.x; i < 16 * kNarrowWin; i += kQThreads) {
+      const int tf = i / kNarrowWin, b = i % kNarrowWin;
+      uint32_t sum = 0;
+#pragma unroll
+      for (int cp = 0; cp < kNarrowCopies; cp++) sum += sn[(cp * 16 + tf) * kNarrowStride + b];
+      sh[(1 + tf) * kHistStride + kHistOff + (b - kNarrowOff)] += sum;
+    }
     __syncthreads();
     constexpr int kBins = EP_NTABLES * kHistStride;
     const int rot = (int)((blockIdx.x * 1031u) % (uint32_t)kBins);
@@ -305,13 +333,14 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
   Raw cw[kRowChunk], nw[kRowChunk];
   uint4 cf[kRowChunk], nf[kRowChunk];
   uint32_t cc[kRowChunk], nc[kRowChunk];
+  // loads past the row's end re-read its last vector (never summed): no branch around a load
+  auto clampv = [&](int64_t m) { return m < vpr ? m : vpr - 1; };
 #pragma unroll
   for (int k = 0; k < kRowChunk; k++) {
-    if (k < vpr) {
-      cw[k] = row_vec<DT, PAD>(w, r, cols, vpr, k);
-      cf[k] = fv[v_row + k];
-      cc[k] = coset[v_row + k];
-    }
+    const int64_t m = clampv(k);
+    cw[k] = row_vec<DT, PAD>(w, r, cols, vpr, m);
+    cf[k] = fv[v_row + m];
+    cc[k] = coset[v_row + m];
   }
   double acc = 0.0;
   int64_t d4 = 0;
@@ -319,11 +348,10 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
     const int64_t v1 = v0 + kRowChunk;
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++) {
-      if (v1 + k < vpr) {
-        nw[k] = row_vec<DT, PAD>(w, r, cols, vpr, v1 + k);
-        nf[k] = fv[v_row + v1 + k];
-        nc[k] = coset[v_row + v1 + k];
-      }
+      const int64_t m = clampv(v1 + k);
+      nw[k] = row_vec<DT, PAD>(w, r, cols, vpr, m);
+      nf[k] = fv[v_row + m];
+      nc[k] = coset[v_row + m];
     }
 #pragma unroll
     for (int k = 0; k < kRowChunk; k++) {

@@ -396,3 +396,33 @@ def test_blob_with_nonfinite_scale_is_rejected(orc):
     bad = blob.copy()
     bad[o:o + 4] = np.array([np.inf], np.float32).view(np.uint8)
     assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_CORRUPT
+
+
+def test_fp8_every_code_in_encoder_kernels(orc):
+    """Rows holding every fp8 e4m3fn code but the two NaNs, at scales from tiny to large, plus a
+    row with a NaN: row sums, quantiser and LS terms against the oracle (the GPU widens fp8 with
+    the hardware conversion, the oracle from the format's definition)."""
+    log("fp8 every code")
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)   # 254 codes
+    g = np.random.Generator(np.random.PCG64(77))
+    rows = [g.permutation(codes) for _ in range(12)]
+    w = np.stack([np.concatenate([r, r[:2]]) for r in rows])                  # 12 x 256
+    ss = gpu_row_sumsq(w, S.FP8)
+    ss_o = orc.row_sumsq(w, S.FP8)
+    assert np.array_equal(ss.view(np.uint64), ss_o.view(np.uint64))
+    for s in (0.05, 1.0, 30.0):
+        gn = orc.gains(ss_o, 256, s)
+        err, cos, fld, hist = gpu_quantize(w, S.FP8, gn)
+        st, cos_o, fld_o = orc.quantize(w, S.FP8, gn)
+        assert (err != 0) == (st != 0)
+        if st == 0:
+            assert np.array_equal(cos, cos_o) and np.array_equal(fld, fld_o)
+            num, den4 = gpu_row_lsq(w, S.FP8, cos_o, fld_o)
+            num_o, den4_o = orc.row_lsq(w, S.FP8, cos_o, fld_o)
+            assert np.array_equal(num.view(np.uint64), num_o.view(np.uint64))
+            assert np.array_equal(den4, den4_o)
+    bad = w.copy()
+    bad[3, 100] = 0x7F                                                         # NaN
+    ss = gpu_row_sumsq(bad, S.FP8)
+    assert np.isnan(ss[3]) and np.isnan(orc.row_sumsq(bad, S.FP8)[3])
+    assert np.array_equal(np.delete(ss, 3).view(np.uint64), np.delete(ss_o, 3).view(np.uint64))
