@@ -43,6 +43,9 @@ def main():
                     help="workload key: 2 (default, the headline line), 3, 4, 5a, 5b, 1")
     ap.add_argument("--refine", type=int, default=5,
                     help="also compress with the per-row refinement (candidates; 0: skip)")
+    ap.add_argument("--consumer-m", type=int, default=0,
+                    help="also time the consumer product X[M x cols] @ W^T with the library "
+                         "GEMM (torch.matmul) on the decoded weight, for this M (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -190,6 +193,28 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # the decode against the product that consumes the weight (prefill / denoiser shapes):
+    # Y[M x rows] = X[M x cols] @ W^T with the library GEMM, W being the decoded matrix
+    consumer = None
+    if args.consumer_m and dt in (S.BF16, S.FP16):
+        Wd = outs[0].view(R, C)
+        X = torch.randn(args.consumer_m, C, device=dev, dtype=torch.float32).to(tdt)
+        for _ in range(3):
+            torch.matmul(X, Wd.t())
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(10):
+            torch.matmul(X, Wd.t())
+        ev1.record()
+        torch.cuda.synchronize()
+        g_ms = ev0.elapsed_time(ev1) / 10
+        flops = 2.0 * args.consumer_m * R * C
+        consumer = {"m": args.consumer_m, "gemm_ms": round(g_ms, 4),
+                    "gemm_tflops": round(flops / (g_ms * 1e-3) / 1e12, 1),
+                    "decode_ms": round(ms, 4),
+                    "decode_over_gemm": round(ms / g_ms, 4)}
+        del X
+
     single = None
     if n_mat > 1:
         # the whole batch: every matrix compressed, then one batched decode per step
@@ -278,6 +303,7 @@ def main():
             "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "refine": refine,
+        "consumer": consumer,
         "encode": {
             "kernel": f"k_encode_tiles<{F // 512}> + offset scan + word copy",
             "ms": round(e_ms, 6), "vectors": nv,
