@@ -538,7 +538,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   if (dtype < EP_BF16 || dtype > EP_FP32) return EP_ERR_DTYPE;
   if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   const uint32_t F = cfg->tile_fields;
-  if (F < 512 || F % 512) return EP_ERR_ARG;
+  if (!device_tile_size(F)) return EP_ERR_ARG;        // the tile sizes the GPU decodes
   const int nc = (int)cfg->refine;
   if (cfg->refine > 9 || (nc > 0 && nc % 2 == 0)) return EP_ERR_ARG;
   if (nc > 0 && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
@@ -745,14 +745,14 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   for (int64_t r = 0; r < rows; r++)
     alpha[r] = den4[r] == 0 ? 0.0f : (float)(num[r] / ((double)den4[r] / 4.0));
 
-  // 6. tiles (device encoder for the tile sizes it takes, else the host encoder), 7. blob
+  // 6. tiles (device encoder), 7. blob
   const int64_t V = F / 8, tiles = (nv + V - 1) / V;
   const int64_t tb = tables_bytes(T.n);
   std::vector<uint32_t> word_off(tiles + 1);
   uint8_t* b = static_cast<uint8_t*>(h_blob);
   Layout L;
   int64_t W;
-  if (device_tile_size(F)) {
+  {
     hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
     if ((st = ep_encode_tiles_gpu(ws.coset, ws.fields, nv, F, &T, ws.enc, ws.enc_bytes,
                                   ws.word_off, ws.max_words, ws.states, ws.words,
@@ -772,25 +772,6 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     hip(hipMemcpyAsync(b + L.words, ws.words, 2 * W, hipMemcpyDeviceToHost, s));
     hip(hipStreamSynchronize(s));
     if (!hip.ok()) return EP_ERR_HIP;
-  } else {
-    std::vector<uint8_t> coset(nv);
-    std::vector<int16_t> fields(8 * nv);
-    hip(hipMemcpyAsync(coset.data(), ws.coset, nv, hipMemcpyDeviceToHost, s));
-    hip(hipMemcpyAsync(fields.data(), ws.fields, 16 * nv, hipMemcpyDeviceToHost, s));
-    hip(hipStreamSynchronize(s));
-    if (!hip.ok()) return EP_ERR_HIP;
-    std::vector<uint32_t> states(tiles * kK);
-    std::vector<uint16_t> words(9 * nv + 1);
-    if ((st = ep_encode_tiles(coset.data(), fields.data(), nv, F, &T, word_off.data(),
-                              states.data(), words.data(), (int64_t)words.size())) != EP_OK)
-      return st;
-    W = word_off[tiles];
-    L = layout(rows, tiles, tb, W);
-    *out_bytes = (size_t)L.total;
-    if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
-    std::memset(b, 0, (size_t)L.total);
-    std::memcpy(b + L.states, states.data(), 4 * kK * tiles);
-    std::memcpy(b + L.words, words.data(), 2 * W);
   }
 
   std::memcpy(b, "EPK1", 4);

@@ -426,3 +426,17 @@ def test_fp8_every_code_in_encoder_kernels(orc):
     ss = gpu_row_sumsq(bad, S.FP8)
     assert np.isnan(ss[3]) and np.isnan(orc.row_sumsq(bad, S.FP8)[3])
     assert np.array_equal(np.delete(ss, 3).view(np.uint64), np.delete(ss_o, 3).view(np.uint64))
+
+
+def test_compress_rejects_undecodable_tile_sizes():
+    import torch
+
+    import entropy_coded_weight_ep_amd as ep
+
+    log("compress tile sizes")
+    t = torch.from_numpy(S.iid_normal(64, 256, seed=3).view(np.int16)).view(torch.bfloat16).cuda()
+    for F in (512, 2048, 12288, 32768):
+        with pytest.raises(ep.EPError):
+            ep.compress(t, ep.LatticeRANSConfig(target_bpp=3.0, tile_fields=F))
+    c = ep.compress(t, ep.LatticeRANSConfig(target_bpp=3.0, tile_fields=16384))
+    assert ep.decompress(c).shape == t.shape
