@@ -16,7 +16,7 @@ UNITS = ["ep_kernels.hip", "ep_decode_bf16.hip", "ep_decode_fp16.hip", "ep_decod
          "ep_decode_int8.hip", "ep_decode_fp32.hip", "ep_encode.hip", "ep_rate.hip", "ep_host.cpp"]
 SOURCES = [os.path.join(CSRC, u) for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "ep.h")] + [
-    os.path.join(CSRC, h) for h in ("ep_internal.h", "ep_device.h", "ep_decode.h")]
+    os.path.join(CSRC, h) for h in ("ep_internal.h", "ep_device.h", "ep_load.h", "ep_decode.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

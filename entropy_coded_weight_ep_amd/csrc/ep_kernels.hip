@@ -17,6 +17,7 @@
 
 #include "ep.h"
 #include "ep_device.h"
+#include "ep_load.h"
 #include "ep_internal.h"
 
 namespace ep {
