@@ -46,6 +46,10 @@ def main():
     ap.add_argument("--consumer-m", type=int, default=0,
                     help="also time the consumer product X[M x cols] @ W^T with the library "
                          "GEMM (torch.matmul) on the decoded weight, for this M (0: skip)")
+    ap.add_argument("--tile-fields", type=int, default=0,
+                    help="override the workload's tile size (4096, 8192 or 16384 fields). "
+                         "Smaller tiles give the decoder more independent rANS states to run "
+                         "at once, and cost 256 B of states per tile")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -63,6 +67,8 @@ def main():
     key = int(args.workload) if args.workload.isdigit() else args.workload
     wl = S.WORKLOADS[key]
     R, C, F, target = wl["rows"], wl["cols"], wl["tile_fields"], wl["target_bpp"]
+    if args.tile_fields:
+        F = args.tile_fields
     dt = wl["dtype"]
     esize = S.ELEM_SIZE[dt]
     tdt = {S.BF16: torch.bfloat16, S.FP16: torch.float16, S.FP8: torch.float8_e4m3fn,
