@@ -403,7 +403,20 @@ def cpu_baseline(blob, out_bytes, min_seconds):
         "sample": f"whole blob decoded {rn} times in {en:.1f} s with its tiles split over "
                   f"{cores} threads; single thread: {one:.4f} GB/s ({r1} decodes in {e1:.1f} s)",
         "single_thread_value": round(one, 4),
+        "cpu": cpu_model(), "host_cpus": os.cpu_count(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty where the file does not exist)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 if __name__ == "__main__":
     main()
