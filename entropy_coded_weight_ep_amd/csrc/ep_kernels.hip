@@ -81,28 +81,31 @@ __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, in
 // for x and for x - 1/2; the closer one wins, coset 0 on ties.  Every operation is a single
 // IEEE fp32 op (no contraction), distances summed e0^2 + e1^2 + ... in index order.
 // ------------------------------------------------------------------------------------------
+// Branch-free: every lane computes the residuals and the worst coordinate, and the move is a
+// select (an odd sum is about every other vector, so a branch would diverge in every wavefront).
+// The residual u - rint(u) is exact and never -0 (x - x rounds to +0), so copysign(1, r_k) is
+// the step towards u, +1 for a zero residual.
 __device__ __forceinline__ void d8_round(const float u[8], float a[8]) {
   int32_t sum = 0;
+  float r[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     a[i] = __builtin_rintf(u[i]);
     sum += (int32_t)a[i];
+    r[i] = __fsub_rn(u[i], a[i]);
   }
-  if (sum & 1) {
-    float r[8];
+  int k = 0;
+  float rk = r[0];                                 // residual of the worst coordinate so far
 #pragma unroll
-    for (int i = 0; i < 8; i++) r[i] = __fsub_rn(u[i], a[i]);
-    int k = 0;
-    float best = __builtin_fabsf(r[0]);
-#pragma unroll
-    for (int i = 1; i < 8; i++) {
-      float d = __builtin_fabsf(r[i]);
-      if (d > best) { best = d; k = i; }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      if (i == k) a[i] = (r[i] >= 0.0f) ? a[i] + 1.0f : a[i] - 1.0f;
+  for (int i = 1; i < 8; i++) {
+    const bool worse = __builtin_fabsf(r[i]) > __builtin_fabsf(rk);
+    rk = worse ? r[i] : rk;
+    k = worse ? i : k;
   }
+  k = (sum & 1) ? k : 8;                           // an even sum moves nothing
+  const float step = __builtin_copysignf(1.0f, rk);
+#pragma unroll
+  for (int i = 0; i < 8; i++) a[i] = (i == k) ? __fadd_rn(a[i], step) : a[i];
 }
 
 __device__ __forceinline__ float sqdist8(const float x[8], const float p[8]) {
@@ -222,12 +225,17 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
     } else {
       float x[8];
       raw_widen<DT>(cur.raw, x);
-      bool out_of_range = false;
+      // !(|x| <= 65536) for all eight at once: the bit patterns without their sign compare
+      // as unsigned integers in the order of |x|, with infinities and NaNs above every finite
+      // value
+      uint32_t mag = 0;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         x[k] = __fmul_rn(x[k], cur.g);
-        out_of_range |= !(__builtin_fabsf(x[k]) <= 65536.0f);
+        const uint32_t b = __float_as_uint(x[k]) << 1;
+        mag = mag > b ? mag : b;
       }
+      bool out_of_range = mag > (0x47800000u << 1);   // 65536.0f
       if (out_of_range) {
 #pragma unroll
         for (int k = 0; k < 8; k++) x[k] = 0.0f;

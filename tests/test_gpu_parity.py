@@ -81,6 +81,62 @@ def test_quantize_range_error(orc):
     assert orc.quantize(w, S.BF16, g)[0] == orc.ERR_RANGE
 
 
+def test_quantize_range_boundary(orc):
+    """The range test |x| <= 65536 at its boundary and on non-finite inputs, one vector per call
+    (the oracle stops at the first vector out of range): the GPU must flag exactly the vectors the
+    oracle rejects and give the oracle's fields for the others.  bf16 holds 65536 and its upper
+    neighbour 65792; fp32 holds 65536's neighbours one ulp away on both sides."""
+    log("quantize range boundary")
+    f32 = lambda b: float(np.array([b], np.uint32).view(np.float32)[0])
+    # the field range |z| <= 32767 rejects |x| = 65536 already; values near 32767 probe that
+    # second boundary (32640 is bf16's largest value below it)
+    specials = [65536.0, 65792.0, f32(0x47800001), f32(0x477FFFFF), np.inf, np.nan,
+                f32(0x7F7FFFFF), f32(0x00000001), 0.0, 1e30,
+                32640.0, 32766.5, 32767.0, 32767.5, 32768.0]
+    rng = np.random.Generator(np.random.PCG64(11))
+    n_ok = n_bad = 0
+    for dt in (S.BF16, S.FP32):
+        for v in specials:
+            for sign in (1.0, -1.0):
+                x = rng.normal(0.0, 3.0, 8).astype(np.float32)
+                x[int(rng.integers(8))] = np.float32(sign * v)
+                w = S.cast_container(x.reshape(1, 8), dt)
+                g = np.ones(1, np.float32)
+                err, cos, fld, _ = gpu_quantize(w, dt, g, with_hist=False)
+                st, cos_o, fld_o = orc.quantize(w, dt, g)
+                assert (err != 0) == (st != 0), (dt, sign * v, err, st)
+                if st == 0:
+                    n_ok += 1
+                    assert np.array_equal(cos, cos_o) and np.array_equal(fld, fld_o)
+                else:
+                    n_bad += 1
+                    assert st == orc.ERR_RANGE and err == 1 << 5
+                    assert cos[0] == 0 and not fld.any()   # flagged vectors are written as 0
+    assert n_ok >= 12 and n_bad >= 24
+
+
+def test_quantize_odd_parity_fixups(orc):
+    """Vectors whose rounded sum is odd for both candidates, with ties in the worst residual
+    (several coordinates at the same distance from their integers, either sign) and zero
+    residuals: the fix-up must move the same coordinate in the same direction as the oracle."""
+    log("quantize parity fix-ups")
+    rng = np.random.Generator(np.random.PCG64(12))
+    rows = []
+    for _ in range(2048):
+        base = rng.integers(-6, 7, 8).astype(np.float32)
+        frac = rng.choice(np.array([0.0, 0.25, -0.25, 0.375, -0.375, 0.125, 0.5, -0.5],
+                                   np.float32), 8)
+        rows.append(base + frac)
+    x = np.stack(rows).astype(np.float32)
+    for dt in (S.BF16, S.FP32):
+        w = S.cast_container(x, dt)
+        g = np.ones(len(rows), np.float32)
+        err, cos, fld, _ = gpu_quantize(w, dt, g, with_hist=False)
+        st, cos_o, fld_o = orc.quantize(w, dt, g)
+        assert err == 0 and st == 0
+        assert np.array_equal(cos, cos_o) and np.array_equal(fld, fld_o)
+
+
 def test_quantize_special_vectors(orc):
     """Hand-worked E8 cases (tests/golden/e8_cases.txt) through the GPU quantiser with unit gain:
     cases that bf16 holds exactly must give the worked answer; all must match the oracle."""
