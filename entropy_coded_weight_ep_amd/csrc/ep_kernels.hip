@@ -85,15 +85,19 @@ __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, in
 // select (an odd sum is about every other vector, so a branch would diverge in every wavefront).
 // The residual u - rint(u) is exact and never -0 (x - x rounds to +0), so copysign(1, r_k) is
 // the step towards u, +1 for a zero residual.
+// The coordinate sum is formed in fp32: the eight rounded values are integers of magnitude at
+// most 65537 (|x| <= 65536 is checked before), so every partial sum is exact and one conversion
+// gives the parity.
 __device__ __forceinline__ void d8_round(const float u[8], float a[8]) {
-  int32_t sum = 0;
+  float fsum = 0.0f;
   float r[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     a[i] = __builtin_rintf(u[i]);
-    sum += (int32_t)a[i];
+    fsum = __fadd_rn(fsum, a[i]);
     r[i] = __fsub_rn(u[i], a[i]);
   }
+  const int32_t sum = (int32_t)fsum;
   int k = 0;
   float rk = r[0];                                 // residual of the worst coordinate so far
 #pragma unroll
@@ -165,17 +169,34 @@ struct QIn {
   bool ok;
 };
 
-template <int DT, bool PAD>
-__device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t rows,
-                                           int64_t cols, const float* __restrict__ gain,
-                                           const int64_t* __restrict__ row_index, uint32_t v,
-                                           uint32_t vpr, double inv_vpr) {
-  QIn<DT> q;
-  // i = v / vpr: fp64 estimate, then one exact correction
+// Where vector v lies: selected row i = v / vpr and vector m = v mod vpr within it.  The first
+// position is divided out exactly (fp64 estimate, one correction); the grid stride then moves it
+// by the constant quotient and remainder of stride / vpr, with one carry.
+struct QPos {
+  uint32_t i, m;
+};
+
+__device__ __forceinline__ QPos q_pos(uint32_t v, uint32_t vpr, double inv_vpr) {
   uint32_t i = (uint32_t)((double)v * inv_vpr);
   const int64_t rem = (int64_t)v - (int64_t)i * vpr;
   i = rem < 0 ? i - 1 : (rem >= (int64_t)vpr ? i + 1 : i);
-  const uint32_t m = v - i * vpr;
+  return QPos{i, v - i * vpr};
+}
+
+__device__ __forceinline__ QPos q_advance(QPos p, QPos step, uint32_t vpr) {
+  p.i += step.i;
+  p.m += step.m;                                   // < 2 vpr: both terms are below vpr
+  const bool carry = p.m >= vpr;
+  return QPos{carry ? p.i + 1 : p.i, carry ? p.m - vpr : p.m};
+}
+
+template <int DT, bool PAD>
+__device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t rows,
+                                           int64_t cols, const float* __restrict__ gain,
+                                           const int64_t* __restrict__ row_index, QPos p,
+                                           uint32_t vpr) {
+  QIn<DT> q;
+  const uint32_t i = p.i, m = p.m;
   const int64_t r = row_index ? row_index[i] : (int64_t)i;
   q.ok = r >= 0 && r < rows;
   q.raw = raw_zero<DT>();
@@ -214,12 +235,15 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
   uint32_t n_c0 = 0, n_c1 = 0;
   const uint32_t stride = gridDim.x * (uint32_t)kQThreads;
   uint32_t v = blockIdx.x * (uint32_t)kQThreads + threadIdx.x;
+  const QPos step = q_pos(stride, vpr, inv_vpr);
+  QPos pos = q_pos(v, vpr, inv_vpr);
   QIn<DT> cur;
-  if (v < n_vec) cur = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, v, vpr, inv_vpr);
+  if (v < n_vec) cur = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, pos, vpr);
   for (; v < n_vec; v += stride) {
     QIn<DT> nxt;
     const bool more = v + stride < n_vec;         // (no overflow: n_vec + stride < 2^32)
-    if (more) nxt = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, v + stride, vpr, inv_vpr);
+    pos = q_advance(pos, step, vpr);               // the position of v + stride
+    if (more) nxt = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, pos, vpr);
     if (!cur.ok) {                                // a row index outside the tensor: skip, report
       bad_row = true;
     } else {
