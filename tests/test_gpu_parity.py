@@ -284,14 +284,14 @@ def test_decode_ring_detects_corrupt_tile(orc):
 
 
 def test_decode_batch_matches_oracle(orc):
-    """One batched decode of 20 blobs (two launches of up to 16; some ragged, some with wide
-    alphabets, different shapes) writes what 20 oracle decodes write."""
+    """One batched decode of 40 blobs (two launches of up to 32; some ragged, some with wide
+    alphabets, different shapes) writes what 40 oracle decodes write."""
     import torch
 
     ep = ep_mod()
     blobs, refs = [], []
     shapes = [(64, 3072), (40, 1000), (96, 512), (8, 8), (128, 1024)]
-    for i in range(20):
+    for i in range(40):
         R, C = shapes[i % len(shapes)]
         key = 4 if i % 3 else 2
         w = S.workload_weights(key, R, C, i)
