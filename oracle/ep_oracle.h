@@ -13,8 +13,9 @@
  * Pins (see tests/test_oracle_*.py): converters vs torch/numpy casts; E8 quantiser vs brute force
  * and the 240-root certificate and the E8 second moment; field map bijection; table-rule worked
  * examples; rANS round trip and size bounds; LS scale closed forms; blob size closed form.
- * The rate search (or_estimate_bpp / or_search_scale) has no pin beyond monotonicity and the
- * achieved-vs-target report: parity unpinned.
+ * The rate search: the estimate (every row sampled) against the information an actual encode
+ * stores (words plus each final state's excess over 2^16), the search against the bracket a
+ * bisection on a monotone estimate must leave.
  */
 #ifndef EP_ORACLE_H
 #define EP_ORACLE_H
