@@ -10,10 +10,11 @@
 //                   unseen value, else max(1, floor(count * 2^P / total)); a deficit goes to the
 //                   most frequent value, an excess is taken from the largest frequencies, lowest
 //                   index first on ties);
-//   k_sum_bits      one wavefront: the sum over tables, then values, of count * (P - log2 f) in
-//                   exactly the host's order, with every product and sum rounded on its own, so
-//                   the result is the host's double bit for bit (P - log2 f comes from a table
-//                   the host fills with its own log2).
+//   k_sum_bits      one workgroup: the products count * (P - log2 f) formed in parallel, then
+//                   summed over tables, then values, by one lane in exactly the host's order,
+//                   with every product and sum rounded on its own, so the result is the host's
+//                   double bit for bit (P - log2 f comes from a table the host fills with its own
+//                   log2).
 // The host finishes the estimate (sampling factor and metadata bytes) from that sum and the
 // tables' sizes.
 #include <hip/hip_runtime.h>
@@ -141,41 +142,86 @@ __global__ __launch_bounds__(kBT) void k_build_tables(const uint32_t* __restrict
 }
 
 // Sum over tables t, then values i < n[t] with a nonzero count, of count * cost[freq], left to
-// right, each product and each sum rounded separately (one wavefront; lanes load 64 values at a
-// time, the sum walks them in order).  The addends are >= 0 and the sum starts at +0, so the
-// values skipped (count 0) would add exactly nothing.
-__global__ __launch_bounds__(64) void k_sum_bits(const uint32_t* __restrict__ hist,
-                                                 const ep_tables* __restrict__ tab,
-                                                 const double* __restrict__ cost,
-                                                 const uint32_t* __restrict__ err,
-                                                 double* __restrict__ bits) {
-  const int lane = threadIdx.x;
+// right, each product and each sum rounded separately.  The entries of all tables are taken as
+// one sequence, in chunks of kSumChunk: the workgroup forms the chunk's products in parallel
+// and packs the nonzero ones into LDS in their order (a ballot rank within each wave, the
+// counts of the waves before it), then one lane adds them to the running sum in that order.
+// The addends are >= 0 and the sum starts at +0, so the entries skipped (count 0) would add
+// exactly nothing: the result is the host's left-to-right sum bit for bit.
+constexpr int kSumThreads = 1024;
+constexpr int kSumChunk = 4 * kSumThreads;
+
+__global__ __launch_bounds__(kSumThreads) void k_sum_bits(const uint32_t* __restrict__ hist,
+                                                          const ep_tables* __restrict__ tab,
+                                                          const double* __restrict__ cost,
+                                                          const uint32_t* __restrict__ err,
+                                                          double* __restrict__ bits) {
+  __shared__ double s_p[kSumChunk];                 // the chunk's nonzero products, in order
+  __shared__ uint32_t s_base[EP_NTABLES + 1];       // first entry of each table
+  __shared__ int32_t s_lo[EP_NTABLES];
+  __shared__ uint32_t s_wave[kSumThreads / 64];     // nonzero products per wave in a pass
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (*err & (1u << EP_ERR_ALPHABET)) {
-    if (lane == 0) *bits = 0.0;
+    if (tid == 0) *bits = 0.0;
     return;
   }
-  double acc = 0.0;
-  for (int t = 0; t < EP_NTABLES; t++) {
-    const uint32_t n = tab->n[t];
-    const uint32_t* c = hist + (size_t)t * EP_HIST_BINS + (tab->lo[t] + 32768);
-    const uint16_t* fq = tab->freq + (size_t)t * EP_HIST_BINS;
-    for (uint32_t b = 0; b < n; b += 64) {
-      const uint32_t i = b + lane;
-      const uint32_t v = i < n ? c[i] : 0u;
-      double p = 0.0;
-      if (v) p = __dmul_rn((double)v, cost[fq[i]]);
-      uint64_t m = __ballot(v != 0u);
-      while (m) {
-        const int k = __builtin_ctzll(m);
-        m &= m - 1;
-        const uint64_t pb = __double_as_longlong(p);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, k);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), k);
-        acc = __dadd_rn(acc, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
-      }
+  if (tid == 0) {
+    uint32_t b = 0;
+    for (int t = 0; t < EP_NTABLES; t++) {
+      s_base[t] = b;
+      s_lo[t] = tab->lo[t];
+      b += tab->n[t];
     }
+    s_base[EP_NTABLES] = b;
   }
-  if (lane == 0) *bits = acc;
+  __syncthreads();
+  const uint32_t total = s_base[EP_NTABLES];
+  double acc = 0.0;                                 // lane 0 of wave 0 keeps the sum
+  for (uint32_t c0 = 0; c0 < total; c0 += kSumChunk) {
+    uint32_t packed = 0;                            // products packed so far in this chunk
+    for (int pass = 0; pass < kSumChunk / kSumThreads; pass++) {
+      const uint32_t e = c0 + (uint32_t)(pass * kSumThreads + tid);
+      double p = 0.0;
+      bool nz = false;
+      if (e < total) {
+        int t = 0;
+        while (e >= s_base[t + 1]) t++;
+        const uint32_t q = e - s_base[t];
+        const uint32_t v = hist[(size_t)t * EP_HIST_BINS + (uint32_t)(s_lo[t] + 32768) + q];
+        if (v) {
+          p = __dmul_rn((double)v, cost[tab->freq[(size_t)t * EP_HIST_BINS + q]]);
+          nz = true;
+        }
+      }
+      const uint64_t m = __ballot(nz);
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (lane == 0) s_wave[wave] = (uint32_t)__popcll(m);
+      __syncthreads();
+      uint32_t before = packed, all = packed;
+      for (int w = 0; w < kSumThreads / 64; w++) {
+        const uint32_t c = s_wave[w];
+        before += w < wave ? c : 0u;
+        all += c;
+      }
+      if (nz) s_p[before + rank] = p;
+      packed = all;
+      __syncthreads();                              // s_wave is rewritten by the next pass
+    }
+    if (tid == 0) {
+      uint32_t i = 0;
+      for (; i + 8 <= packed; i += 8) {
+        double v[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = s_p[i + k];
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc = __dadd_rn(acc, v[k]);
+      }
+      for (; i < packed; i++) acc = __dadd_rn(acc, s_p[i]);
+    }
+    __syncthreads();                                // s_p is rewritten by the next chunk
+  }
+  if (tid == 0) *bits = acc;
 }
 
 // Rate of row blockIdx.x in units of 2^-16 bit under the device tables: the sum over its vectors
@@ -308,7 +354,7 @@ bool estimate_enqueue(const ep_hist* d_hist, void* d_workspace, bool upload_cost
                          hipMemcpyHostToDevice, s) == hipSuccess;
   k_zero_u32<<<1, 1, 0, s>>>(w.err);
   k_build_tables<<<EP_NTABLES, kBT, 0, s>>>(d_hist->counts, w.tables, w.err);
-  k_sum_bits<<<1, 64, 0, s>>>(d_hist->counts, w.tables, w.cost, w.err, w.bits);
+  k_sum_bits<<<1, kSumThreads, 0, s>>>(d_hist->counts, w.tables, w.cost, w.err, w.bits);
   ok &= hipGetLastError() == hipSuccess;
   ok &= hipMemcpyAsync(h_bits, w.bits, 8, hipMemcpyDeviceToHost, s) == hipSuccess;
   ok &= hipMemcpyAsync(h_err, w.err, 4, hipMemcpyDeviceToHost, s) == hipSuccess;
