@@ -767,7 +767,10 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     L = layout(rows, tiles, tb, W);
     *out_bytes = (size_t)L.total;
     if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
-    std::memset(b, 0, (size_t)L.total);
+    // zero what the copies below do not write: every section before the states (their padding
+    // included) and the words section's tail padding; the states fill their section exactly
+    std::memset(b, 0, (size_t)L.states);
+    std::memset(b + L.words + 2 * W, 0, (size_t)(L.total - L.words - 2 * W));
     hip(hipMemcpyAsync(b + L.states, ws.states, 4 * kK * tiles, hipMemcpyDeviceToHost, s));
     hip(hipMemcpyAsync(b + L.words, ws.words, 2 * W, hipMemcpyDeviceToHost, s));
     hip(hipStreamSynchronize(s));
