@@ -1,12 +1,14 @@
 """GPU edge cases of the whole library path (compress on the device, blob byte-identical to the
 oracle's, decode bit-identical): degenerate shapes, a matrix whose payload is empty, a constant
-matrix, one huge row, and a zero row among normal ones."""
+matrix, one huge row, and a zero row among normal ones; and every GPU call repeated on the same
+inputs gives the same bytes."""
 
 import numpy as np
 import pytest
 
 import ep_synth as S
-from gpu_util import GpuBlob, gpu_compress, log
+from gpu_util import (GpuBlob, ep_mod, gpu_compress, gpu_quantize, gpu_row_lsq, gpu_row_sumsq,
+                      log)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +51,44 @@ def test_zero_rows_among_others(orc):
     w = S.lognormal_rows(50, 1024, seed=91)
     w[[0, 7, 49]] = 0
     _roundtrip(orc, w, S.BF16, 4.0, 8192)
+
+
+def test_every_call_is_deterministic():
+    """Each GPU call run twice on the same inputs gives the same bytes: the quantiser's cosets,
+    fields and histogram (integer atomics in any order), the fp64 row sums and LS terms (one
+    lane per row, fixed order), the whole library compress (rate search, tables, tile encoder)
+    with and without the per-row refinement, and the single and batched decodes."""
+    import torch
+
+    ep = ep_mod()
+    log("determinism")
+    w = S.workload_weights(2, 300, 1000, 0)             # ragged width, several tiles
+    ss1, ss2 = gpu_row_sumsq(w, S.BF16), gpu_row_sumsq(w, S.BF16)
+    assert np.array_equal(ss1.view(np.uint64), ss2.view(np.uint64))
+    g = (1.0 / (np.sqrt(ss1 / 1000.0) * 0.3)).astype(np.float32)
+    q1, q2 = gpu_quantize(w, S.BF16, g), gpu_quantize(w, S.BF16, g)
+    for a, b in zip(q1, q2):
+        assert np.array_equal(np.asarray(a), np.asarray(b))
+    assert q1[0] == 0
+    l1, l2 = gpu_row_lsq(w, S.BF16, q1[1], q1[2]), gpu_row_lsq(w, S.BF16, q1[1], q1[2])
+    assert np.array_equal(l1[0].view(np.uint64), l2[0].view(np.uint64))
+    assert np.array_equal(l1[1], l2[1])
+    for refine in (0, 5):
+        b1, s1 = gpu_compress(w, S.BF16, 3.5, 8192, refine=refine)
+        b2, s2 = gpu_compress(w, S.BF16, 3.5, 8192, refine=refine)
+        assert s1 == s2 and np.array_equal(b1, b2)
+    blob, _ = gpu_compress(w, S.BF16, 3.5, 8192)
+    gb = GpuBlob(blob)
+    e1, o1 = gb.decode()
+    e2, o2 = gb.decode()
+    assert e1 == 0 and e2 == 0 and np.array_equal(o1, o2)
+    outs = [torch.zeros(gb.out_bytes(), dtype=torch.uint8, device="cuda") for _ in range(3)]
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        assert ep.ep_decompress_batch([gb.d_blob] * 3, [gb.info] * 3, [gb.d_tab] * 3, outs,
+                                      d_err) == 0
+        torch.cuda.synchronize()
+        assert int(d_err.item()) == 0
+        for o in outs:
+            got = o.cpu().numpy().view(np.uint16).reshape(300, gb.pitch())[:, :1000]
+            assert np.array_equal(got, o1)
