@@ -1,7 +1,7 @@
 """GPU edge cases of the whole library path (compress on the device, blob byte-identical to the
 oracle's, decode bit-identical): degenerate shapes, a matrix whose payload is empty, a constant
-matrix, one huge row, and a zero row among normal ones; and every GPU call repeated on the same
-inputs gives the same bytes."""
+matrix, one huge row, and a zero row among normal ones; every GPU call repeated on the same
+inputs gives the same bytes; and bad inputs to compress return the oracle's status."""
 
 import numpy as np
 import pytest
@@ -92,3 +92,44 @@ def test_every_call_is_deterministic():
         for o in outs:
             got = o.cpu().numpy().view(np.uint16).reshape(300, gb.pitch())[:, :1000]
             assert np.array_equal(got, o1)
+
+
+def _lib_status(w, dt, target, F, force_scale=0.0):
+    ep = ep_mod()
+    try:
+        gpu_compress(w, dt, target, F, force_scale=force_scale)
+    except ep.EPError as e:
+        return e.status
+    return 0
+
+
+def test_compress_failures_match_oracle(orc):
+    """Failure injection through the whole library compress: each bad input returns the status
+    the oracle returns for it (non-finite input, target rate outside its range or NaN, a scale
+    that pushes the lattice coordinates past the field range, one that gives a field more
+    distinct values than the 2^12 slots of its table), and the library stays usable."""
+    log("compress failures")
+    w = S.workload_weights(2, 64, 1024, 0)
+    nan_w, inf_w = w.copy(), w.copy()
+    nan_w[5, 17] = 0x7FC0                                    # bf16 NaN
+    inf_w[60, 1000] = 0xFF80                                 # bf16 -inf
+    wide = S.iid_normal(512, 1024, seed=9)                   # 65536 vectors
+    cases = [
+        (nan_w, 3.0, 0.0, "nan input"),
+        (inf_w, 3.0, 0.0, "inf input"),
+        (w, 0.0005, 0.0, "target below range"),
+        (w, 11.5, 0.0, "target above range"),
+        (w, float("nan"), 0.0, "nan target"),
+        (w, 3.0, 1e-7, "coordinates past the field range"),
+        (wide, 3.0, 1.0 / 3000.0, "too many distinct values"),
+    ]
+    seen = set()
+    for x, target, fs, what in cases:
+        st_o = orc.compress(x, S.BF16, target, 8192, force_s=fs)[0]
+        st_l = _lib_status(x, S.BF16, target, 8192, force_scale=fs)
+        assert st_o != 0 and st_l == st_o, (what, st_l, st_o)
+        seen.add(st_o)
+    assert {orc.ERR_NONFINITE, orc.ERR_ARG, orc.ERR_RANGE, orc.ERR_ALPHABET} <= seen
+    blob, _ = gpu_compress(w, S.BF16, 3.0, 8192)            # still works afterwards
+    st, blob_o, _ = orc.compress(w, S.BF16, 3.0, 8192)
+    assert st == 0 and np.array_equal(blob, blob_o)
