@@ -16,12 +16,12 @@
 // offsets, and a copy writes every stack reversed into the blob's word stream.
 //
 // Per symbol: entry (f, cum) of value - lo in the table of this phase and coset; flush
-// x & 0xFFFF when x >= f * 2^20; then x = (x / f) * 2^12 + x mod f + cum.  x / f: the fp64
-// product of x and a reciprocal of f, truncated, then corrected exactly by one step either way
-// from the integer remainder.  The hardware fp64 reciprocal is only good to about 2^-23
-// relative; one Newton step squares that to about 2^-46, so for x < 2^32 the estimate is off by
-// less than 2^-13 and the one-step correction is exact.  The step has no branch: lanes without
-// a vector keep their state.
+// x & 0xFFFF when x >= f * 2^20; then x = (x / f) * 2^12 + x mod f + cum.  x / f: the fp32
+// product of x and the hardware reciprocal of f, truncated, then corrected exactly by one step
+// either way from the integer remainder.  After the flush x < f * 2^20, so the quotient is below
+// 2^20; rounding x to fp32 (2^-24), the reciprocal (1 ulp, 2^-23) and the product (2^-24) put
+// the estimate within 2^-22 relative, under 1/4 absolute, and the one-step correction is exact.
+// The step has no branch: lanes without a vector keep their state.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
       const bool ok = !valid || (in && (e & 0x1FFFu) != 0u);
       bad |= ok ? 0u : 1u;
       const bool use = valid && ok;
-      const uint32_t f = use ? (e & 0x1FFFu) : 1u;
+      // lanes that encode nothing divide by 2^12 (result discarded): every quotient < 2^20
+      const uint32_t f = use ? (e & 0x1FFFu) : 4096u;
       const uint32_t cum = e >> 13;
       const bool flush = use && (uint64_t)x >= ((uint64_t)f << (32 - EP_PRECISION));
       const uint64_t m = __ballot(flush);
@@ -133,10 +134,10 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
       sp += (uint32_t)__popcll(m);
       {
         const uint32_t xs = flush ? x >> 16 : x;
-        const double fd = (double)f;
-        double rc = __builtin_amdgcn_rcp(fd);
-        rc = __builtin_fma(__builtin_fma(-fd, rc, 1.0), rc, rc);
-        uint32_t q = (uint32_t)((double)xs * rc);
+        // quotient estimate in fp32: xs < f 2^20, so xs / f < 2^20; the conversion of xs, the
+        // hardware reciprocal (1 ulp) and the product err by at most ~2^-22 relative, i.e. by
+        // less than 1/4 in absolute terms, and one integer step either way makes it exact
+        uint32_t q = (uint32_t)(__fmul_rn((float)xs, __builtin_amdgcn_rcpf((float)f)));
         int32_t r = (int32_t)(xs - q * f);
         q = r < 0 ? q - 1u : (r >= (int32_t)f ? q + 1u : q);
         r = r < 0 ? r + (int32_t)f : (r >= (int32_t)f ? r - (int32_t)f : r);
