@@ -212,3 +212,30 @@ def test_refine_select_matches_oracle(ep, orc, seed):
         lam_o, sel_o = orc.refine_select(D, Rq, budget)
         assert np.float64(lam).view(np.uint64) == np.float64(lam_o).view(np.uint64)
         assert np.array_equal(sel, sel_o)
+
+
+def test_encoder_quotient_estimate_bound():
+    """The device tile encoder divides x by the frequency f (1..4096) with an fp32 estimate
+    (x rounded to fp32, times the hardware reciprocal, which is within 1 ulp of 1/f), truncated,
+    then corrected by a single integer step.  That is exact only if the truncated estimate is
+    never more than 1 away from floor(x / f) while x < f * 2^20: swept here for every f, with
+    the reciprocal rounded correctly and off by one ulp either way, at the largest quotients,
+    around every multiple of f there, and at random ones."""
+    f = np.arange(1, 4097, dtype=np.int64)
+    rc0 = (np.float32(1.0) / f.astype(np.float32)).astype(np.float32)
+    worst = 0
+    rng = np.random.default_rng(5)
+    ff = rng.integers(1, 4097, 500_000)
+    xr = (rng.random(500_000) * ff * (1 << 20)).astype(np.int64)
+    for rc in (rc0, np.nextafter(rc0, np.float32(0)), np.nextafter(rc0, np.float32(np.inf))):
+        for k in list(range((1 << 20) - 16, 1 << 20)) + [0, 1, 2, 65535, 65536]:
+            for d in (-1, 0, 1):
+                x = k * f + d
+                ok = (x >= 0) & (x < f * (1 << 20))
+                q = (x[ok].astype(np.float32) * rc[ok]).astype(np.float32)
+                est = np.floor(q.astype(np.float64)).astype(np.int64)
+                worst = max(worst, int(np.abs(est - x[ok] // f[ok]).max()))
+        q = (xr.astype(np.float32) * rc[ff - 1]).astype(np.float32)
+        est = np.floor(q.astype(np.float64)).astype(np.int64)
+        worst = max(worst, int(np.abs(est - xr // ff).max()))
+    assert worst <= 1
