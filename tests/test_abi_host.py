@@ -232,6 +232,8 @@ def test_encoder_quotient_estimate_bound():
             for d in (-1, 0, 1):
                 x = k * f + d
                 ok = (x >= 0) & (x < f * (1 << 20))
+                if not ok.any():
+                    continue
                 q = (x[ok].astype(np.float32) * rc[ok]).astype(np.float32)
                 est = np.floor(q.astype(np.float64)).astype(np.int64)
                 worst = max(worst, int(np.abs(est - x[ok] // f[ok]).max()))
