@@ -21,7 +21,8 @@
 // either way from the integer remainder.  After the flush x < f * 2^20, so the quotient is below
 // 2^20; rounding x to fp32 (2^-24), the reciprocal (1 ulp, 2^-23) and the product (2^-24) put
 // the estimate within 2^-22 relative, under 1/4 absolute, and the one-step correction is exact.
-// The step has no branch: lanes without a vector keep their state.
+// The step has no branch: a lane without a vector divides by 2^12 and adds 0, which leaves its
+// state as it was.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,15 +70,16 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
   const uint32_t tv = t * V;
   const uint32_t nvt = n_vec - tv < V ? n_vec - tv : V;
 
-  // the lane's vectors: packed fields and coset bits
+  // the lane's vectors (j < nj): packed fields and coset bits
+  const uint32_t nj = nvt > (uint32_t)lane ? (nvt - (uint32_t)lane + 63u) >> 6 : 0u;
   uint4 fk[J];
   uint32_t cbits = 0;
   uint32_t bad = 0;                                 // a symbol outside its table
 #pragma unroll
   for (int j = 0; j < J; j++) {
-    const uint32_t u = (uint32_t)lane + 64u * j;
     fk[j] = make_uint4(0, 0, 0, 0);
-    if (u < nvt) {
+    if ((uint32_t)j < nj) {
+      const uint32_t u = (uint32_t)lane + 64u * j;
       fk[j] = reinterpret_cast<const uint4*>(fields)[tv + u];
       const uint32_t cb = coset[tv + u];
       bad |= cb > 1u ? 1u : 0u;
@@ -96,31 +98,41 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
     int t0 = phase == 0 ? 0 : phase;
     int t1 = phase == 0 ? 0 : 8 + phase;
     asm volatile("" : "+s"(t0), "+s"(t1));
-    const int32_t lo0 = ta.lo[t0], lo1 = ta.lo[t1];
-    const uint32_t n0 = ta.n[t0], n1 = ta.n[t1];
-    const uint32_t off0 = ta.off[t0], off1 = ta.off[t1];
+    // a value's entry is at value + (off - lo) of its coset's table; coset 1's parameters are
+    // copied to vector registers once per phase so that one bitfield insert picks them per lane
+    const uint32_t lo0 = (uint32_t)ta.lo[t0], n0 = ta.n[t0], d0 = ta.off[t0] - lo0;
+    uint32_t lo1 = (uint32_t)ta.lo[t1], n1 = ta.n[t1], d1 = ta.off[t1] - lo1;
+    asm volatile("" : "+v"(lo1), "+v"(n1), "+v"(d1));
 #pragma unroll
     for (int j = J - 1; j >= 0; --j) {
-      const bool valid = (uint32_t)lane + 64u * j < nvt;
-      const uint32_t c = (cbits >> j) & 1u;
+      // 0 or ~0, opaque so that the selects below stay bitfield inserts on vector registers
+      // (left alone, the compiler keeps every vector's coset as a lane mask in scalar registers
+      // across the unrolled loop and spills them)
+      uint32_t cm = (uint32_t)__builtin_amdgcn_sbfe((int32_t)cbits, j, 1);
+      asm volatile("" : "+v"(cm));
       int32_t value;
-      if (phase == 0) value = (int32_t)c;
+      if (phase == 0) value = (int32_t)(cm & 1u);
       else value = field_of(fk[j], phase - 1);
-      const uint32_t s = (uint32_t)(value - (c ? lo1 : lo0));
-      const uint32_t nt = c ? n1 : n0;
-      const bool in = s < nt;                       // (an empty table has nt = 0)
+      const uint32_t lo = (lo1 & cm) | (lo0 & ~cm);
+      const uint32_t nt = (n1 & cm) | (n0 & ~cm);
+      const uint32_t d = (d1 & cm) | (d0 & ~cm);
+      const bool in = (uint32_t)value - lo < nt;    // (an empty table has nt = 0)
       // an in-range index always (entry 0 of the packed array when the value is not in the table)
-      const uint32_t idx = in ? (c ? off1 : off0) + s : 0u;
+      const uint32_t idx = in ? (uint32_t)value + d : 0u;
       uint32_t e;
       if constexpr (LDS_TAB) e = s_ent[idx];
       else e = ent[idx];
-      const bool ok = !valid || (in && (e & 0x1FFFu) != 0u);
-      bad |= ok ? 0u : 1u;
-      const bool use = valid && ok;
-      // lanes that encode nothing divide by 2^12 (result discarded): every quotient < 2^20
-      const uint32_t f = use ? (e & 0x1FFFu) : 4096u;
-      const uint32_t cum = e >> 13;
-      const bool flush = use && (uint64_t)x >= ((uint64_t)f << (32 - EP_PRECISION));
+      const uint32_t fr = e & 0x1FFFu;
+      const bool valid = (uint32_t)j < nj;
+      const bool use = valid && in && fr != 0u;
+      bad |= (valid && !use) ? 1u : 0u;
+      asm volatile("" : "+v"(bad));                 // or-ed in now, not kept as lane masks
+      // lanes that encode nothing take f = 2^12 and cum = 0: they never flush (x >> 20 < 2^12),
+      // and the update below gives back x itself, (x / 2^12) 2^12 + x mod 2^12
+      const uint32_t f = use ? fr : 4096u;
+      uint32_t cum = use ? e >> 13 : 0u;
+      asm volatile("" : "+v"(cum));                 // chosen here: the mask dies before the flush
+      const bool flush = (x >> 20) >= f;            // x >= f 2^20
       const uint64_t m = __ballot(flush);
       if (flush) {
         // emission index: the flushing lanes above this one come first
@@ -141,8 +153,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
         int32_t r = (int32_t)(xs - q * f);
         q = r < 0 ? q - 1u : (r >= (int32_t)f ? q + 1u : q);
         r = r < 0 ? r + (int32_t)f : (r >= (int32_t)f ? r - (int32_t)f : r);
-        const uint32_t xn = (q << EP_PRECISION) + (uint32_t)r + cum;
-        x = use ? xn : x;
+        x = (q << EP_PRECISION) + (uint32_t)r + cum;
       }
     }
   }
