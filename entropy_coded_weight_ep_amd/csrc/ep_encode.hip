@@ -45,14 +45,29 @@ struct EncTabs {
   int32_t lo[EP_NTABLES];
 };
 
-// Field k (0..7) of a vector's packed fields (eight int16, two per word).
+// Field k (0..7) of a vector's packed fields: eight int16, two per word, or eight int8, four
+// per word.
 __device__ __forceinline__ int32_t field_of(const uint4& q, int k) {
   const uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
   return (k & 1) ? (int32_t)w >> 16 : (int32_t)(int16_t)(w & 0xFFFFu);
 }
+__device__ __forceinline__ int32_t field_of(const uint2& q, int k) {
+  return __builtin_amdgcn_sbfe((int32_t)(k < 4 ? q.x : q.y), 8 * (k & 3), 8);
+}
 
-template <int J, bool LDS_TAB>
-__global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
+// BYTES: every field table lies within [-128, 127], so the lane's fields are held as bytes, two
+// registers per vector instead of four (a field that does not fit a byte is an alphabet error,
+// reported like any value outside its table).
+// Waves per SIMD the registers are budgeted for (the compiler fits the kernel to 512 / waves).
+template <int J, bool BYTES>
+struct EncOcc {
+  static constexpr int waves = J <= 8 ? 8 : (J <= 16 ? (BYTES ? 5 : 4) : (BYTES ? 3 : 2));
+};
+
+template <int J, bool LDS_TAB, bool BYTES>
+__global__ __launch_bounds__(64 * kEncWaves)
+__attribute__((amdgpu_waves_per_eu(EncOcc<J, BYTES>::waves, EncOcc<J, BYTES>::waves)))
+void k_encode_tiles(
     const uint8_t* __restrict__ coset, const int16_t* __restrict__ fields, uint32_t n_vec,
     uint32_t tiles, const uint32_t* __restrict__ ent, uint32_t n_ent, EncTabs ta,
     uint32_t* __restrict__ counts, uint32_t* __restrict__ states, uint16_t* __restrict__ stack,
@@ -72,18 +87,32 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
 
   // the lane's vectors (j < nj): packed fields and coset bits
   const uint32_t nj = nvt > (uint32_t)lane ? (nvt - (uint32_t)lane + 63u) >> 6 : 0u;
-  uint4 fk[J];
+  using Packed = typename std::conditional<BYTES, uint2, uint4>::type;
+  Packed fk[J];
   uint32_t cbits = 0;
   uint32_t bad = 0;                                 // a symbol outside its table
 #pragma unroll
   for (int j = 0; j < J; j++) {
-    fk[j] = make_uint4(0, 0, 0, 0);
+    uint4 q = make_uint4(0, 0, 0, 0);
     if ((uint32_t)j < nj) {
       const uint32_t u = (uint32_t)lane + 64u * j;
-      fk[j] = reinterpret_cast<const uint4*>(fields)[tv + u];
+      q = reinterpret_cast<const uint4*>(fields)[tv + u];
       const uint32_t cb = coset[tv + u];
       bad |= cb > 1u ? 1u : 0u;
       cbits |= (cb & 1u) << j;
+    }
+    if constexpr (BYTES) {
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int32_t v = __builtin_amdgcn_sbfe((int32_t)w[k >> 1], 16 * (k & 1), 16);
+        bad |= v == __builtin_amdgcn_sbfe(v, 0, 8) ? 0u : 1u;
+      }
+      // the low byte of each field: f0 f1 f2 f3 | f4 f5 f6 f7
+      fk[j] = make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
+                         __builtin_amdgcn_perm(q.w, q.z, 0x06040200u));
+    } else {
+      fk[j] = q;
     }
   }
 
@@ -112,7 +141,7 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode_tiles(
       asm volatile("" : "+v"(cm));
       int32_t value;
       if (phase == 0) value = (int32_t)(cm & 1u);
-      else value = field_of(fk[j], phase - 1);
+      else value = field_of(fk[j], phase - 1);     // (byte or half of the packed fields)
       const uint32_t lo = (lo1 & cm) | (lo0 & ~cm);
       const uint32_t nt = (n1 & cm) | (n0 & ~cm);
       const uint32_t d = (d1 & cm) | (d0 & ~cm);
@@ -223,14 +252,13 @@ __global__ __launch_bounds__(256) void k_copy_words(const uint16_t* __restrict__
   }
 }
 
-template <int J, bool LDS_TAB>
+template <int J, bool LDS_TAB, bool BYTES>
 static void launch_enc(dim3 grid, size_t lds, hipStream_t s, const uint8_t* coset,
                        const int16_t* fields, uint32_t nv, uint32_t tiles, const uint32_t* ent,
                        uint32_t n_ent, const EncTabs& ta, uint32_t* counts, uint32_t* states,
                        uint16_t* stack, uint32_t* err) {
-  k_encode_tiles<J, LDS_TAB><<<grid, 64 * kEncWaves, lds, s>>>(coset, fields, nv, tiles, ent,
-                                                               n_ent, ta, counts, states, stack,
-                                                               err);
+  k_encode_tiles<J, LDS_TAB, BYTES><<<grid, 64 * kEncWaves, lds, s>>>(
+      coset, fields, nv, tiles, ent, n_ent, ta, counts, states, stack, err);
 }
 
 // Workspace layout: packed table entries, tile counts, per-tile word stacks (9V words each).
@@ -309,10 +337,20 @@ extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* 
   const dim3 grid((tiles + kEncWaves - 1) / kEncWaves);
   const bool lds_tab = n_ent <= kEncLdsEntries;
   const size_t lds = lds_tab ? 4 * (size_t)n_ent : 0;
+  // every field table (1..16) within [-128, 127]: the kernel holds the fields as bytes
+  bool bytes = true;
+  for (int t = 1; t < EP_NTABLES; t++)
+    if (ta.n[t] && (ta.lo[t] < -128 || (int64_t)ta.lo[t] + (int64_t)ta.n[t] - 1 > 127))
+      bytes = false;
   auto go = [&](auto jc, auto lc) {
-    launch_enc<decltype(jc)::value, decltype(lc)::value>(grid, lds, s, d_coset, d_fields, nv,
-                                                          tiles, ws.ent, n_ent, ta, ws.counts,
-                                                          d_states, ws.stack, d_err);
+    if (bytes)
+      launch_enc<decltype(jc)::value, decltype(lc)::value, true>(
+          grid, lds, s, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
+          ws.stack, d_err);
+    else
+      launch_enc<decltype(jc)::value, decltype(lc)::value, false>(
+          grid, lds, s, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
+          ws.stack, d_err);
   };
   using T8 = std::integral_constant<int, 8>;
   using T16 = std::integral_constant<int, 16>;

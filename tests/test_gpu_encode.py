@@ -108,6 +108,24 @@ def test_encode_tiles_symbol_outside_table(orc):
     assert st == 0 and err & (1 << ERR_ALPHABET)
 
 
+@pytest.mark.parametrize("F", [4096, 8192, 16384])
+def test_encode_tiles_value_outside_a_byte(orc, F):
+    """Tables that fit [-128, 127] let the kernel hold the fields as bytes.  A field value that
+    does not fit a byte must still be an alphabet error, even where its low byte would alias a
+    value of the table (257 and -255 both truncate to 1), as the oracle reports."""
+    log("encode byte aliasing", F)
+    ep = ep_mod()
+    cos, fld = _symbols(orc, 2, 16, 2048, 0.3)
+    lo, n, freq = _tables(orc, cos, fld)
+    assert all(lo[t] >= -128 and lo[t] + n[t] - 1 <= 127 for t in range(1, 17) if n[t])
+    for v in (257, -255, 300):
+        bad = fld.copy()
+        bad[8 * 700 + 2] = v
+        assert orc.encode_tiles(cos, bad, F, 64, 12, lo, n, freq)[0] != 0
+        st, err, *_ = gpu_encode_tiles(cos, bad, F, ep.tables_struct(lo, n, freq))
+        assert st == 0 and err & (1 << ERR_ALPHABET), (v, err)
+
+
 def test_encode_tiles_word_capacity(orc):
     log("encode capacity")
     ep = ep_mod()
