@@ -2,6 +2,6 @@
 #include "ep_decode.h"
 
 namespace ep {
-template hipError_t launch_decode<EP_FP32>(const DecodeArgs&, int, bool, bool, bool, bool,
+template hipError_t launch_decode<EP_FP32>(const DecodeArgs&, int, bool, bool, bool, bool, bool,
                                            int, size_t, hipStream_t);
 }  // namespace ep

@@ -53,11 +53,14 @@ struct DecodeArgs {
 
 // Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).
 // `slow`: scale without the fused multiply-add (needed for bf16 when some row scale is tiny).
+// `rows2`: every blob has at least 64 J vectors per row (a tile spans at most two rows), so the
+// kernel keeps two row scales per wave instead of one per vector (used with wide alphabets at
+// J = 32, where it lets 3 waves per SIMD fit the registers).
 // `ring`: stream each tile's words through an LDS ring of words_stride words (a power of two)
 // instead of holding the whole tile.
 template <int DT>
-hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool ring,
-                         int waves, size_t lds, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
+                         bool ring, int waves, size_t lds, hipStream_t s);
 
 // Device part of the rate estimate (ep_rate.hip): enqueue on `s` the table build of d_hist and
 // the coded-bit sum of its symbols into the rate workspace (the cost table is copied in when

@@ -602,7 +602,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   if (i0.tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
   // batch-wide choices: the largest tile, any wide alphabet, any tiny row scale
   uint32_t maxw = 0;
-  bool big = false, slow = false;
+  bool big = false, slow = false, long_rows = true;
   int64_t total_tiles = 0;
   for (int i = 0; i < n; i++) {
     const ep_blob_info& in = infos[i];
@@ -617,6 +617,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
         in.tiles != (nv_in + J * 64 - 1) / (J * 64))
       return EP_ERR_SHAPE;
     maxw = std::max(maxw, in.max_tile_words);
+    long_rows &= (in.cols + 7) / 8 >= (int64_t)J * 64;   // a tile spans at most two rows
     big |= in.big_alphabet != 0;
     slow |= in.tiny_scale != 0;
     total_tiles += in.tiles;
@@ -636,22 +637,27 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
   // per wave 256 B of states and the words region.  Waves per workgroup and layout: the choice
   // that keeps the most tiles resident at once; ties go to the linear layout, then to the smaller
-  // workgroup (spread over more CUs).
+  // workgroup (spread over more CUs) of at least 4 waves.
   const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
   auto lds_of = [&](int w, uint32_t stride) {
     return lds_tables + (size_t)w * (256 + (size_t)stride * 2);
   };
   // waves per SIMD the decoder's registers allow: 8, 4 and 4 for 8, 16 and 32 vectors per lane
-  // (2 at 32 with wide alphabets, whose fields take 16 bits each)
-  const int occ = J <= 8 ? 8 : (J <= 16 ? 4 : (big ? 2 : 4));
+  // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
+  // tile's vectors twice over and two row scales per wave replace one per vector)
+  const bool rows2 = J == 32 && big && long_rows;
+  const int occ = J <= 8 ? 8 : (J <= 16 ? 4 : (big ? (rows2 ? 3 : 2) : 4));
   const int64_t waves_per_cu = 4 * occ;
-  const int max_waves = occ >= 4 ? kDecWaves : kDecWaves / 2;
+  const int max_waves = occ >= 4 ? kDecWaves : (occ == 3 ? 12 : kDecWaves / 2);
   int waves = 0;
   bool ring = false;
   uint32_t stride = 0;
   int64_t best = -1;
-  // candidates: linear (ties go to it, and among its sizes to the smaller workgroup), then the
-  // full ring and the half ring, each taken only when it keeps strictly more tiles resident
+  // candidates: linear (ties go to it, and among its sizes to the smaller workgroup down to 4
+  // waves, below which each wave would load a large share of the tables itself), then the full
+  // ring and the half ring, each taken only when it keeps strictly more tiles resident.  The
+  // count of resident tiles is capped at the tiles there are (a partly filled last workgroup
+  // adds none).
   for (int lay = 0; lay < 3; lay++) {
     const bool rg = lay >= 1;
     if (layout == EP_DECODE_LINEAR && rg) continue;
@@ -659,13 +665,13 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     if (lay == 2 && ring_half == ring_stride) continue;
     const uint32_t st = lay == 0 ? lin_stride : (lay == 1 ? ring_stride : ring_half);
     if (rg && layout == 0 && st >= lin_stride) continue;
-    for (int w = max_waves; w >= 1; w >>= 1) {
-      if ((int64_t)lds_of(w, st) > kLdsPerCU) continue;
+    for (const int w : {16, 12, 8, 4, 2, 1}) {
+      if (w > max_waves || (int64_t)lds_of(w, st) > kLdsPerCU) continue;
       const int64_t per_cu =
           std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, st), waves_per_cu / w);
       const int64_t grid = (total_tiles + w - 1) / w;
-      const int64_t resident = std::min(grid, kCUs * per_cu) * w;
-      if (resident > best || (resident == best && !rg)) {
+      const int64_t resident = std::min(std::min(grid, kCUs * per_cu) * w, total_tiles);
+      if (resident > best || (resident == best && !rg && w >= 4)) {
         best = resident;
         waves = w;
         ring = rg;
@@ -684,13 +690,13 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     if (a.n == 0) return EP_OK;
     hipError_t e;
     switch (i0.dtype) {
-      case EP_BF16: e = launch_decode<EP_BF16>(a, J, big, ragged, slow, ring, waves, lds, s); break;
-      case EP_FP16: e = launch_decode<EP_FP16>(a, J, big, ragged, false, ring, waves, lds, s); break;
+      case EP_BF16: e = launch_decode<EP_BF16>(a, J, big, ragged, slow, rows2, ring, waves, lds, s); break;
+      case EP_FP16: e = launch_decode<EP_FP16>(a, J, big, ragged, false, rows2, ring, waves, lds, s); break;
       case EP_FP8_E4M3FN:
-        e = launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, ring, waves, lds, s);
+        e = launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, rows2, ring, waves, lds, s);
         break;
-      case EP_FP32: e = launch_decode<EP_FP32>(a, J, big, ragged, slow, ring, waves, lds, s); break;
-      default: e = launch_decode<EP_INT8>(a, J, big, ragged, false, ring, waves, lds, s); break;
+      case EP_FP32: e = launch_decode<EP_FP32>(a, J, big, ragged, slow, rows2, ring, waves, lds, s); break;
+      default: e = launch_decode<EP_INT8>(a, J, big, ragged, false, rows2, ring, waves, lds, s); break;
     }
     a.n = 0;
     return e == hipSuccess ? EP_OK : EP_ERR_HIP;

@@ -496,3 +496,62 @@ def test_compress_rejects_undecodable_tile_sizes():
             ep.compress(t, ep.LatticeRANSConfig(target_bpp=3.0, tile_fields=F))
     c = ep.compress(t, ep.LatticeRANSConfig(target_bpp=3.0, tile_fields=16384))
     assert ep.decompress(c).shape == t.shape
+
+
+# Rows of at least 64 * 32 vectors with wide alphabets at 16384-field tiles: the decoder keeps
+# two row scales per wave (a tile then spans at most two rows) and runs 12-wave workgroups.
+LONG_ROWS = [
+    ("5b", 16, 28672, 6.0),      # int8, tiles crossing rows
+    ("5b", 7, 16400, 6.0),       # 2050 vectors per row, ragged last tile
+    (3, 9, 16384, 7.0),          # fp16, exactly 2048 vectors per row
+    (2, 5, 20000, 8.0),          # bf16
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS)
+def test_decode_long_rows_wide_alphabet(orc, case):
+    key, R, C, target = case
+    ep = ep_mod()
+    log("decode long rows", case)
+    w = S.workload_weights(key, R, C)
+    dt = S.WORKLOADS[key]["dtype"]
+    st, blob, _ = orc.compress(w, dt, target, 16384)
+    assert st == 0
+    st, ref, _, _ = orc.decompress(blob)
+    assert st == 0
+    gb = GpuBlob(blob)
+    assert gb.info.big_alphabet and (C + 7) // 8 >= 2048
+    for flags in (None, ep.EP_DECODE_LINEAR, ep.EP_DECODE_RING, ep.EP_DECODE_RING_MIN):
+        err, out = gb.decode(flags=flags)
+        assert err == 0 and np.array_equal(out, ref), flags
+
+
+def test_decode_batch_long_rows(orc):
+    """Two long-row wide-alphabet blobs in one batched call (the two-row path), and the same two
+    with a short-row blob added (the per-vector scales): all as the oracle writes them."""
+    import torch
+
+    ep = ep_mod()
+    log("decode batch long rows")
+    cases = [("5b", 16, 28672, 6.0, 0), ("5b", 7, 16400, 6.0, 1), ("5b", 24, 2048, 6.0, 2)]
+    blobs, refs = [], []
+    for key, R, C, target, i in cases:
+        w = S.workload_weights(key, R, C, i)
+        st, blob, _ = orc.compress(w, S.WORKLOADS[key]["dtype"], target, 16384)
+        assert st == 0
+        st, ref, _, _ = orc.decompress(blob)
+        assert st == 0
+        blobs.append(GpuBlob(blob))
+        refs.append(ref)
+    for sel in ([0, 1], [0, 1, 2]):
+        outs = [torch.zeros(blobs[i].out_bytes(), dtype=torch.uint8, device="cuda") for i in sel]
+        d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        st = ep.ep_decompress_batch([blobs[i].d_blob for i in sel], [blobs[i].info for i in sel],
+                                    [blobs[i].d_tab for i in sel], outs, d_err)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert int(d_err.item()) == 0
+        for i, o in zip(sel, outs):
+            b = blobs[i]
+            got = o.cpu().numpy().view(np.int8).reshape(b.info.rows, b.pitch())[:, :b.info.cols]
+            assert np.array_equal(got, refs[i])
