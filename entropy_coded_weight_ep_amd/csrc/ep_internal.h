@@ -14,8 +14,9 @@ struct TableArgs {
   int32_t lo[EP_NTABLES];
 };
 
-// Largest number of wavefronts (= tiles) per decoder workgroup (16 for up to 16 vectors per
-// lane, 8 for 32); the launcher picks 16, 8, 4, 2 or 1 from LDS, registers and the tile count.
+// Largest number of wavefronts (= tiles) per decoder workgroup: 16 where the registers allow 4
+// or more waves per SIMD, 12 at 3 and 8 at 2.  The launcher picks 16, 12, 8, 4, 2 or 1 from LDS,
+// registers and the tile count.
 constexpr int kDecWaves = 16;
 // Compute units of an MI355X and LDS bytes per CU, for the decoder's workgroup size choice.
 constexpr int64_t kCUs = 256;
