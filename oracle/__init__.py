@@ -64,6 +64,11 @@ def lib():
             "or_histogram": (None, [P, P, i64, P]),
             "or_normalize": (i32, [P, C.c_int32, i32, P]),
             "or_build_tables": (i32, [P, i32, P, P, P]),
+            "or_build_tables_ex": (i32, [P, i32, i32, P, P, P]),
+            "or_escape_keep": (None, [P, i32, P]),
+            "or_substitute": (i32, [i32, C.c_uint32, P]),
+            "or_exceptions": (i64, [P, P, i64, P, P, P, P, P]),
+            "or_blob_exceptions": (i32, [P, i64, P]),
             "or_row_lsq": (None, [i32, P, i64, i64, P, P, P, P]),
             "or_alpha": (C.c_float, [dbl, i64]),
             "or_encode_tiles": (i32, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, i64]),
@@ -197,6 +202,50 @@ def build_tables(counts: np.ndarray, precision: int = 12):
     st = lib().or_build_tables(_p(np.ascontiguousarray(counts, np.uint64)), precision, _p(lo),
                                _p(n), _p(freq))
     return st, lo, n, freq
+
+
+def build_tables_escapes(counts: np.ndarray, precision: int = 12):
+    """Tables with escapes allowed: a field table with more than 2^P distinct values keeps the
+    2^P most frequent ones."""
+    lo = np.empty(NTABLES, np.int32)
+    n = np.empty(NTABLES, np.uint32)
+    freq = np.zeros((NTABLES, NBINS), np.uint16)
+    st = lib().or_build_tables_ex(_p(np.ascontiguousarray(counts, np.uint64)), precision, 1,
+                                  _p(lo), _p(n), _p(freq))
+    return st, lo, n, freq
+
+
+def escape_keep(counts_one_table: np.ndarray, precision: int = 12) -> np.ndarray:
+    kept = np.zeros(NBINS, np.uint8)
+    lib().or_escape_keep(_p(np.ascontiguousarray(counts_one_table, np.uint64)), precision,
+                         _p(kept))
+    return kept.astype(bool)
+
+
+def substitute(lo: int, n: int, freq_one_table: np.ndarray) -> int:
+    return lib().or_substitute(int(lo), int(n), _p(np.ascontiguousarray(freq_one_table, np.uint16)))
+
+
+def exceptions(cos, fld, lo, n, freq):
+    """(idx = v | coset << 31, true fields [X, 8]) of the vectors with an escaped field."""
+    cos = np.ascontiguousarray(cos, np.uint8)
+    fld = np.ascontiguousarray(fld, np.int16)
+    lo = np.ascontiguousarray(lo, np.int32)
+    n = np.ascontiguousarray(n, np.uint32)
+    freq = np.ascontiguousarray(freq, np.uint16)
+    m = lib().or_exceptions(_p(cos), _p(fld), cos.size, _p(lo), _p(n), _p(freq), None, None)
+    idx = np.zeros(max(m, 1), np.uint32)
+    xf = np.zeros((max(m, 1), 8), np.int16)
+    lib().or_exceptions(_p(cos), _p(fld), cos.size, _p(lo), _p(n), _p(freq), _p(idx), _p(xf))
+    return idx[:m], xf[:m]
+
+
+def blob_exceptions(blob: np.ndarray) -> int:
+    m = C.c_int64()
+    st = lib().or_blob_exceptions(_p(blob), blob.size, C.byref(m))
+    if st:
+        raise ValueError(f"oracle blob parse failed: {st}")
+    return m.value
 
 
 def row_lsq(w: np.ndarray, dtype: int, cos: np.ndarray, fld: np.ndarray):

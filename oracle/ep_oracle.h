@@ -16,6 +16,8 @@
  * The rate search: the estimate (every row sampled) against the information an actual encode
  * stores (words plus each final state's excess over 2^16), the search against the bracket a
  * bisection on a monotone estimate must leave.
+ * Escapes: the kept set against a brute-force ranking; a blob with escapes decodes to the
+ * direct reconstruction of the quantised vectors (the coding is lossless whatever it escapes).
  */
 #ifndef EP_ORACLE_H
 #define EP_ORACLE_H
@@ -61,6 +63,13 @@ void or_histogram(const uint8_t* coset, const int16_t* fields, int64_t nv, uint6
 int or_normalize(const uint64_t* counts, int32_t n, int precision, uint16_t* freq);
 int or_build_tables(const uint64_t* counts, int precision, int32_t* lo, uint32_t* n,
                     uint16_t* freq /* [17][65536] */);
+/* escapes != 0: a field table with more than 2^P distinct values keeps the 2^P most frequent */
+int or_build_tables_ex(const uint64_t* counts, int precision, int escapes, int32_t* lo,
+                       uint32_t* n, uint16_t* freq);
+void or_escape_keep(const uint64_t* counts /* one table */, int precision, uint8_t* kept);
+int32_t or_substitute(int32_t lo, uint32_t n, const uint16_t* freq /* one table */);
+int64_t or_exceptions(const uint8_t* coset, const int16_t* fields, int64_t nv, const int32_t* lo,
+                      const uint32_t* n, const uint16_t* freq, uint32_t* idx, int16_t* xf);
 
 /* row least squares */
 void or_row_lsq(int dt, const void* w, int64_t rows, int64_t cols, const uint8_t* coset,
@@ -72,6 +81,10 @@ int or_encode_tiles(const uint8_t* coset, const int16_t* fields, int64_t nv, int
                     int lanes, int precision, const int32_t* lo, const uint32_t* n,
                     const uint16_t* freq, uint32_t* word_off, uint32_t* states, uint16_t* words,
                     int64_t words_cap);
+int or_encode_tiles_ex(const uint8_t* coset, const int16_t* fields, int64_t nv, int tile_fields,
+                       int lanes, int precision, const int32_t* lo, const uint32_t* n,
+                       const uint16_t* freq, int substitute, uint32_t* word_off, uint32_t* states,
+                       uint16_t* words, int64_t words_cap);
 int or_decode_tiles(const uint32_t* word_off, const uint32_t* states, const uint16_t* words,
                     int64_t nv, int tile_fields, int lanes, int precision, const int32_t* lo,
                     const uint32_t* n, const uint16_t* freq, int64_t t0, int64_t t1,
@@ -87,6 +100,7 @@ int or_decompress(const uint8_t* blob, int64_t bytes, int64_t t0, int64_t t1, vo
 int or_blob_fields(const uint8_t* blob, int64_t bytes, int64_t* rows, int64_t* cols, int* dt,
                    int* tile_fields, int64_t* tiles, double* s, int64_t* payload_words,
                    int64_t* table_bytes);
+int or_blob_exceptions(const uint8_t* blob, int64_t bytes, int64_t* n_exc);
 double or_estimate_bpp(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
                        int tile_fields, double s);
 double or_search_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
