@@ -32,6 +32,7 @@
 
 #include "ep.h"
 #include "ep_device.h"
+#include "ep_internal.h"
 
 namespace ep {
 
@@ -292,13 +293,13 @@ extern "C" size_t ep_encode_workspace_bytes(int64_t n_vectors, uint32_t tile_fie
   return enc_carve(nullptr, n_vectors, tile_fields).total;
 }
 
-extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* d_fields,
-                                         int64_t n_vectors, uint32_t tile_fields,
-                                         const ep_tables* h_tables, void* d_workspace,
-                                         size_t workspace_bytes, uint32_t* d_word_off,
-                                         uint32_t* d_max_tile_words, uint32_t* d_states,
-                                         uint16_t* d_words, int64_t words_cap, uint32_t* d_err,
-                                         void* stream) {
+namespace ep {
+
+ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
+                           uint32_t tile_fields, const ep_tables* h_tables, bool substitute,
+                           void* d_workspace, size_t workspace_bytes, uint32_t* d_word_off,
+                           uint32_t* d_max_tile_words, uint32_t* d_states, uint16_t* d_words,
+                           int64_t words_cap, uint32_t* d_err, hipStream_t s) {
   if (!d_coset || !d_fields || !h_tables || !d_workspace || !d_word_off || !d_max_tile_words ||
       !d_states || !d_words || !d_err || words_cap < 0)
     return EP_ERR_ARG;
@@ -307,7 +308,6 @@ extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* 
   const int J = (int)(tile_fields / (8 * EP_LANES));
   if (tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_ARG;
   if (workspace_bytes < ep_encode_workspace_bytes(n_vectors, tile_fields)) return EP_ERR_CAPACITY;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const uint32_t nv = (uint32_t)n_vectors;
   const uint32_t V = tile_fields / 8;
   const uint32_t tiles = (uint32_t)((n_vectors + V - 1) / V);
@@ -328,6 +328,21 @@ extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* 
       cum += f;
     }
     if (ta.n[t] && cum != (1u << EP_PRECISION)) return EP_ERR_ARG;
+    if (substitute && t >= 1 && ta.n[t] > 0) {
+      // widen the field table to every int16 value: a value it lacks takes the entry of its
+      // substitute, the most probable value (the lowest on ties)
+      const uint16_t* f = h_tables->freq + (size_t)t * EP_HIST_BINS;
+      uint32_t best = 0;
+      for (uint32_t i = 1; i < ta.n[t]; i++)
+        if (f[i] > f[best]) best = i;
+      std::vector<uint32_t> wide(EP_HIST_BINS, ent[ta.off[t] + best]);
+      for (uint32_t i = 0; i < ta.n[t]; i++)
+        if (f[i]) wide[(size_t)(ta.lo[t] + 32768) + i] = ent[ta.off[t] + i];
+      ent.resize(ta.off[t]);
+      ent.insert(ent.end(), wide.begin(), wide.end());
+      ta.lo[t] = -32768;
+      ta.n[t] = EP_HIST_BINS;
+    }
   }
   if (ent.empty()) ent.push_back(0);
   const uint32_t n_ent = (uint32_t)ent.size();
@@ -366,4 +381,143 @@ extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* 
                                     (uint64_t)words_cap, d_err);
   k_copy_words<<<tiles, 256, 0, s>>>(ws.stack, 9 * V, d_word_off, d_words, (uint64_t)words_cap);
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+// Exception list: whether vector v has a field its table lacks, from per-table bitmaps of the
+// kept values (table 1 + t: 2048 words, bit value + 32768).
+__device__ __forceinline__ bool has_escape(const uint8_t* __restrict__ coset,
+                                           const uint4* __restrict__ fields,
+                                           const uint32_t* __restrict__ keep, uint32_t v,
+                                           uint32_t& c, uint4& q) {
+  c = coset[v] & 1u;
+  q = fields[v];
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  bool esc = false;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const uint32_t bin = ((k & 1) ? (w[k >> 1] >> 16) : w[k >> 1]) + 32768u;   // int16 + 32768
+    const uint32_t b = bin & 0xFFFFu;
+    const uint32_t word = keep[(8u * c + (uint32_t)k) * 2048u + (b >> 5)];
+    esc |= ((word >> (b & 31u)) & 1u) == 0u;
+  }
+  return esc;
+}
+
+constexpr int kExcThreads = 256;
+
+__global__ __launch_bounds__(kExcThreads) void k_exc_count(const uint8_t* __restrict__ coset,
+                                                          const uint4* __restrict__ fields,
+                                                          uint32_t nv,
+                                                          const uint32_t* __restrict__ keep,
+                                                          uint32_t* __restrict__ counts) {
+  __shared__ uint32_t s_n[kExcThreads / 64];
+  const uint32_t v = blockIdx.x * kExcThreads + threadIdx.x;
+  uint32_t c;
+  uint4 q;
+  const bool esc = v < nv && has_escape(coset, fields, keep, v, c, q);
+  const uint64_t m = __ballot(esc);
+  if ((threadIdx.x & 63) == 0) s_n[threadIdx.x >> 6] = (uint32_t)__popcll(m);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < kExcThreads / 64; i++) t += s_n[i];
+    counts[blockIdx.x] = t;
+  }
+}
+
+// Writes the block's entries in vector order from its first position offsets[block].
+__global__ __launch_bounds__(kExcThreads) void k_exc_write(const uint8_t* __restrict__ coset,
+                                                          const uint4* __restrict__ fields,
+                                                          uint32_t nv,
+                                                          const uint32_t* __restrict__ keep,
+                                                          const uint32_t* __restrict__ offsets,
+                                                          uint32_t* __restrict__ idx,
+                                                          uint4* __restrict__ xf) {
+  __shared__ uint32_t s_n[kExcThreads / 64];
+  const uint32_t v = blockIdx.x * kExcThreads + threadIdx.x;
+  uint32_t c = 0;
+  uint4 q;
+  const bool esc = v < nv && has_escape(coset, fields, keep, v, c, q);
+  const uint64_t m = __ballot(esc);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_n[wave] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t pos = offsets[blockIdx.x];
+  for (int i = 0; i < wave; i++) pos += s_n[i];
+  pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (esc) {
+    idx[pos] = v | (c << 31);
+    xf[pos] = q;
+  }
+}
+
+ep_status find_exceptions(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
+                          uint32_t tile_fields, const ep_tables* h_tables, void* d_workspace,
+                          size_t workspace_bytes, void* d_scratch, std::vector<uint32_t>& idx,
+                          std::vector<uint8_t>& fields, hipStream_t s) {
+  if (!d_coset || !d_fields || !h_tables || !d_workspace || !d_scratch) return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
+  if (n_vectors < 1 || n_vectors >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
+  if (workspace_bytes < ep_encode_workspace_bytes(n_vectors, tile_fields)) return EP_ERR_CAPACITY;
+  const EncWs ws = enc_carve(d_workspace, n_vectors, tile_fields);
+  const uint32_t nv = (uint32_t)n_vectors;
+  const uint32_t blocks = (nv + kExcThreads - 1) / kExcThreads;
+  // kept-value bitmaps in the entry region; the list's indices, then the block counts, in the
+  // tile stacks' region (at least 18 bytes per vector); the fields in d_scratch
+  std::vector<uint32_t> keep((size_t)16 * 2048, 0u);
+  for (int t = 1; t < EP_NTABLES; t++) {
+    const uint16_t* f = h_tables->freq + (size_t)t * EP_HIST_BINS;
+    for (uint32_t i = 0; i < h_tables->n[t]; i++)
+      if (f[i]) {
+        const uint32_t b = (uint32_t)(h_tables->lo[t] + 32768) + i;
+        keep[(size_t)(t - 1) * 2048 + (b >> 5)] |= 1u << (b & 31u);
+      }
+  }
+  uint32_t* d_idx = reinterpret_cast<uint32_t*>(ws.stack);
+  uint32_t* d_counts = d_idx + ((size_t)nv + 63) / 64 * 64;
+  std::vector<uint32_t> counts(blocks);
+  const uint4* f4 = reinterpret_cast<const uint4*>(d_fields);
+  bool ok = hipMemcpyAsync(ws.ent, keep.data(), 4 * keep.size(), hipMemcpyHostToDevice, s) ==
+            hipSuccess;
+  k_exc_count<<<blocks, kExcThreads, 0, s>>>(d_coset, f4, nv, ws.ent, d_counts);
+  ok &= hipMemcpyAsync(counts.data(), d_counts, 4 * (size_t)blocks, hipMemcpyDeviceToHost, s) ==
+        hipSuccess;
+  ok &= hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) return EP_ERR_HIP;
+  uint32_t total = 0;
+  for (uint32_t b = 0; b < blocks; b++) {
+    const uint32_t c = counts[b];
+    counts[b] = total;
+    total += c;
+  }
+  idx.assign(total, 0u);
+  fields.assign((size_t)16 * total, 0u);
+  if (total == 0) return EP_OK;
+  ok &= hipMemcpyAsync(d_counts, counts.data(), 4 * (size_t)blocks, hipMemcpyHostToDevice, s) ==
+        hipSuccess;
+  k_exc_write<<<blocks, kExcThreads, 0, s>>>(d_coset, f4, nv, ws.ent, d_counts, d_idx,
+                                             static_cast<uint4*>(d_scratch));
+  ok &= hipMemcpyAsync(idx.data(), d_idx, 4 * (size_t)total, hipMemcpyDeviceToHost, s) ==
+        hipSuccess;
+  ok &= hipMemcpyAsync(fields.data(), d_scratch, 16 * (size_t)total, hipMemcpyDeviceToHost, s) ==
+        hipSuccess;
+  ok &= hipStreamSynchronize(s) == hipSuccess;
+  return ok && hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+}  // namespace ep
+
+extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* d_fields,
+                                         int64_t n_vectors, uint32_t tile_fields,
+                                         const ep_tables* h_tables, void* d_workspace,
+                                         size_t workspace_bytes, uint32_t* d_word_off,
+                                         uint32_t* d_max_tile_words, uint32_t* d_states,
+                                         uint16_t* d_words, int64_t words_cap, uint32_t* d_err,
+                                         void* stream) {
+  ep::clear_pending_error();
+  return ep::encode_tiles_dev(d_coset, d_fields, n_vectors, tile_fields, h_tables, false,
+                              d_workspace, workspace_bytes, d_word_off, d_max_tile_words,
+                              d_states, d_words, words_cap, d_err,
+                              static_cast<hipStream_t>(stream));
 }

@@ -36,17 +36,21 @@ int64_t tables_bytes(const uint32_t* n) {
 }
 
 struct Layout {
-  int64_t tables, alpha, word_off, states, words, total;
+  int64_t tables, alpha, word_off, states, words, exc_idx, exc_fields, total;
 };
 
-Layout layout(int64_t rows, int64_t tiles, int64_t table_bytes, int64_t words) {
+// Sections in blob order; a blob with escapes (version 1.1) ends with its exception list: the
+// indices u32[n_exc], then the fields i16[n_exc][8].
+Layout layout(int64_t rows, int64_t tiles, int64_t table_bytes, int64_t words, int64_t n_exc = 0) {
   Layout L;
   L.tables = kHeaderBytes;
   L.alpha = L.tables + table_bytes;
   L.word_off = L.alpha + round16(4 * rows);
   L.states = L.word_off + round16(4 * (tiles + 1));
   L.words = L.states + round16(4 * (int64_t)kK * tiles);
-  L.total = L.words + round16(2 * words);
+  L.exc_idx = L.words + round16(2 * words);
+  L.exc_fields = L.exc_idx + round16(4 * n_exc);
+  L.total = n_exc > 0 ? L.exc_fields + 16 * n_exc : L.exc_idx;
   return L;
 }
 
@@ -181,12 +185,10 @@ extern "C" void ep_config_default(ep_config* cfg) {
   cfg->force_scale = 0.0;
 }
 
-extern "C" ep_status ep_build_tables(const ep_hist* h_hist, uint32_t precision_bits,
-                                     ep_tables* h_out) {
-  if (!h_hist || !h_out) return EP_ERR_ARG;
-  if (precision_bits != EP_PRECISION) return EP_ERR_ARG;
-  for (int t = 0; t < EP_NTABLES; t++) {
-    const uint32_t* c = h_hist->counts + (size_t)t * EP_HIST_BINS;
+namespace {
+// Table t of h_out from its counts c (EP_HIST_BINS bins).
+ep_status build_table(const uint32_t* c, int t, ep_tables* h_out) {
+  {
     int first = -1, last = -1;
     for (int b = 0; b < EP_HIST_BINS; b++) {
       if (c[b]) {
@@ -198,11 +200,46 @@ extern "C" ep_status ep_build_tables(const ep_hist* h_hist, uint32_t precision_b
     if (first < 0) {
       h_out->lo[t] = 0;
       h_out->n[t] = 0;
-      continue;
+      return EP_OK;
     }
     h_out->lo[t] = first - 32768;
     h_out->n[t] = (uint32_t)(last - first + 1);
-    const ep_status st = normalise(c + first, h_out->n[t], f);
+    return normalise(c + first, h_out->n[t], f);
+  }
+}
+
+// Tables with escapes: a field table whose counts hold more than M distinct values keeps the M
+// most frequent (larger count first, lower value on ties) and is built over those alone; its
+// other values are escaped (coded as the table's substitute and listed as exceptions).
+ep_status build_tables_escaped(const ep_hist* h_hist, ep_tables* h_out) {
+  std::vector<uint32_t> kept(EP_HIST_BINS);
+  std::vector<std::pair<uint32_t, int>> order;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    const uint32_t* c = h_hist->counts + (size_t)t * EP_HIST_BINS;
+    order.clear();
+    for (int b = 0; b < EP_HIST_BINS; b++)
+      if (c[b]) order.emplace_back(c[b], b);
+    if (t >= 1 && order.size() > (size_t)kM) {
+      std::sort(order.begin(), order.end(), [](const auto& x, const auto& y) {
+        return x.first != y.first ? x.first > y.first : x.second < y.second;
+      });
+      std::fill(kept.begin(), kept.end(), 0u);
+      for (uint32_t i = 0; i < kM; i++) kept[order[i].second] = order[i].first;
+      c = kept.data();
+    }
+    const ep_status st = build_table(c, t, h_out);
+    if (st != EP_OK) return st;
+  }
+  return EP_OK;
+}
+}  // namespace
+
+extern "C" ep_status ep_build_tables(const ep_hist* h_hist, uint32_t precision_bits,
+                                     ep_tables* h_out) {
+  if (!h_hist || !h_out) return EP_ERR_ARG;
+  if (precision_bits != EP_PRECISION) return EP_ERR_ARG;
+  for (int t = 0; t < EP_NTABLES; t++) {
+    const ep_status st = build_table(h_hist->counts + (size_t)t * EP_HIST_BINS, t, h_out);
     if (st != EP_OK) return st;
   }
   return EP_OK;
@@ -242,6 +279,7 @@ extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t c
 extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64_t cols,
                                       int64_t n_sample_rows, uint32_t tile_fields,
                                       void* d_workspace, size_t workspace_bytes, void* stream) {
+  ep::clear_pending_error();
   if (!d_hist || !d_workspace || rows < 1 || cols < 1 || n_sample_rows < 1 || tile_fields < 8)
     return INFINITY;
   if (workspace_bytes < ep_estimate_workspace_bytes()) return INFINITY;
@@ -361,7 +399,7 @@ extern "C" ep_status ep_compress_bound(int64_t rows, int64_t cols, uint32_t tile
   const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
   uint32_t nmax[EP_NTABLES];
   for (int t = 0; t < EP_NTABLES; t++) nmax[t] = 65535;
-  *bytes = (size_t)layout(rows, tiles, tables_bytes(nmax), 9 * nv).total;
+  *bytes = (size_t)layout(rows, tiles, tables_bytes(nmax), 9 * nv, nv).total;
   return EP_OK;
 }
 
@@ -439,9 +477,8 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   if (!h_blob || !out) return EP_ERR_ARG;
   const uint8_t* b = static_cast<const uint8_t*>(h_blob);
   if (bytes < (size_t)kHeaderBytes || std::memcmp(b, "EPK1", 4) != 0) return EP_ERR_CORRUPT;
-  uint16_t version;
-  std::memcpy(&version, b + 4, 2);
-  if (version != 1) return EP_ERR_VERSION;
+  // version 1.0, or 1.1 for a blob that lists escaped vectors
+  if (b[4] != 1 || b[5] > 1) return EP_ERR_VERSION;
   ep_blob_info I;
   std::memset(&I, 0, sizeof I);
   I.dtype = b[6];
@@ -466,8 +503,19 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   const int64_t nv = I.rows * ((I.cols + 7) / 8), V = I.tile_fields / 8;
   if (I.tiles != (nv + V - 1) / V) return EP_ERR_CORRUPT;
   if (I.payload_words < 0 || I.payload_words > ((int64_t)1 << 32)) return EP_ERR_CORRUPT;
-  const Layout L = layout(I.rows, I.tiles, tb, I.payload_words);
+  uint32_t n_exc;
+  std::memcpy(&n_exc, b + 60, 4);
+  if ((b[5] == 0) != (n_exc == 0) || (int64_t)n_exc > nv) return EP_ERR_CORRUPT;
+  const Layout L = layout(I.rows, I.tiles, tb, I.payload_words, n_exc);
   if ((int64_t)bytes != L.total) return EP_ERR_CORRUPT;
+  // the exception list names vectors in increasing order, each inside the tensor
+  for (uint32_t i = 0; i < n_exc; i++) {
+    uint32_t e, prev = 0;
+    std::memcpy(&e, b + L.exc_idx + 4 * (int64_t)i, 4);
+    if (i > 0) std::memcpy(&prev, b + L.exc_idx + 4 * (int64_t)(i - 1), 4);
+    const int64_t v = e & 0x7FFFFFFFu;
+    if (v >= nv || (i > 0 && v <= (int64_t)(prev & 0x7FFFFFFFu))) return EP_ERR_CORRUPT;
+  }
   int64_t p = L.tables;
   bool big = false;
   for (int t = 0; t < EP_NTABLES; t++) {
@@ -526,6 +574,9 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   I.off_word_off = L.word_off;
   I.off_states = L.states;
   I.off_words = L.words;
+  I.n_exceptions = n_exc;
+  I.off_exceptions = n_exc > 0 ? L.exc_idx : 0;
+  I.off_exception_fields = n_exc > 0 ? L.exc_fields : 0;
   *out = I;
   return EP_OK;
 }
@@ -534,6 +585,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
                                  const ep_config* cfg, void* d_workspace, size_t workspace_bytes,
                                  void* h_blob, size_t cap, size_t* out_bytes, double* scale_out,
                                  void* stream) {
+  ep::clear_pending_error();
   if (!d_w || !cfg || !d_workspace || !h_blob || !out_bytes) return EP_ERR_ARG;
   if (dtype < EP_BF16 || dtype > EP_FP32) return EP_ERR_DTYPE;
   if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
@@ -723,6 +775,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   std::vector<int64_t> den4(rows);
   std::vector<ep_tables> tabv(1);
   ep_tables& T = tabv[0];
+  bool escapes = false;
   {
     const ep_status q = quantise_with(final_gains.data(), true);
     if (q != EP_OK) return q == EP_ERR_HIP ? EP_ERR_HIP : EP_ERR_ARG;
@@ -739,8 +792,25 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     if (!hip.ok()) return EP_ERR_HIP;
     if (err_host & (1u << EP_ERR_RANGE)) return EP_ERR_RANGE;
     if (err_host & ~(1u << EP_ERR_ALPHABET)) return EP_ERR_ARG;
-    if (err_host) return EP_ERR_ALPHABET;
+    if (err_host) {
+      // some field table holds more than M distinct values: build the tables with escapes on
+      // the host from the full histogram
+      std::vector<ep_hist> hh(1);
+      hip(hipMemcpyAsync(hh.data(), ws.hist, sizeof(ep_hist), hipMemcpyDeviceToHost, s));
+      hip(hipStreamSynchronize(s));
+      if (!hip.ok()) return EP_ERR_HIP;
+      if ((st = build_tables_escaped(hh.data(), &T)) != EP_OK) return st;
+      escapes = true;
+    }
   }
+  // the exception list: the vectors with a field their table lacks
+  std::vector<uint32_t> x_idx;
+  std::vector<uint8_t> x_fields;
+  if (escapes &&
+      (st = ep::find_exceptions(ws.coset, ws.fields, nv, F, &T, ws.enc, ws.enc_bytes, ws.words,
+                                x_idx, x_fields, s)) != EP_OK)
+    return st;
+  const int64_t n_exc = (int64_t)x_idx.size();
   std::vector<float> alpha(rows);
   for (int64_t r = 0; r < rows; r++)
     alpha[r] = den4[r] == 0 ? 0.0f : (float)(num[r] / ((double)den4[r] / 4.0));
@@ -754,9 +824,9 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   int64_t W;
   {
     hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
-    if ((st = ep_encode_tiles_gpu(ws.coset, ws.fields, nv, F, &T, ws.enc, ws.enc_bytes,
-                                  ws.word_off, ws.max_words, ws.states, ws.words,
-                                  9 * nv + 1, ws.err, stream)) != EP_OK)
+    if ((st = ep::encode_tiles_dev(ws.coset, ws.fields, nv, F, &T, escapes, ws.enc,
+                                   ws.enc_bytes, ws.word_off, ws.max_words, ws.states, ws.words,
+                                   9 * nv + 1, ws.err, s)) != EP_OK)
       return st;
     hip(hipMemcpyAsync(word_off.data(), ws.word_off, 4 * (tiles + 1), hipMemcpyDeviceToHost, s));
     hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
@@ -764,7 +834,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     if (!hip.ok()) return EP_ERR_HIP;
     if (err_host) return EP_ERR_ARG;
     W = word_off[tiles];
-    L = layout(rows, tiles, tb, W);
+    L = layout(rows, tiles, tb, W, n_exc);
     *out_bytes = (size_t)L.total;
     if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
     // zero what the copies below do not write: every section before the states (their padding
@@ -778,8 +848,8 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   }
 
   std::memcpy(b, "EPK1", 4);
-  const uint16_t version = 1;
-  std::memcpy(b + 4, &version, 2);
+  b[4] = 1;                                           // version 1.0, or 1.1 with escapes
+  b[5] = n_exc > 0 ? 1 : 0;
   b[6] = (uint8_t)dtype;
   b[7] = EP_PRECISION;
   const uint64_t r64 = (uint64_t)rows, c64 = (uint64_t)cols, w64 = (uint64_t)W;
@@ -795,6 +865,12 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   std::memcpy(b + 40, &sc, 8);
   std::memcpy(b + 48, &w64, 8);
   std::memcpy(b + 56, &maxw, 4);
+  const uint32_t x32 = (uint32_t)n_exc;
+  std::memcpy(b + 60, &x32, 4);
+  if (n_exc > 0) {
+    std::memcpy(b + L.exc_idx, x_idx.data(), 4 * (size_t)n_exc);
+    std::memcpy(b + L.exc_fields, x_fields.data(), 16 * (size_t)n_exc);
+  }
   int64_t p = L.tables;
   for (int t = 0; t < EP_NTABLES; t++) {
     std::memcpy(b + p, &T.lo[t], 4);

@@ -3,9 +3,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "ep.h"
 
 namespace ep {
+
+// Clears an error that an earlier HIP call outside the library left pending.  Every entry point
+// that launches kernels calls it first: its launch checks (hipGetLastError after a launch) then
+// report only its own launches.
+inline void clear_pending_error() { (void)hipGetLastError(); }
 
 // Byte offsets (into the blob) and sizes of the 17 table records, for table expansion.
 struct TableArgs {
@@ -62,6 +69,31 @@ struct DecodeArgs {
 template <int DT>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
                          bool ring, int waves, size_t lds, hipStream_t s);
+
+// Rewrites a blob's escaped vectors after its tiles are decoded (ep_decode_<dtype>.hip): idx and
+// xf are the exception list on the device (n entries), alpha the blob's row scales.
+template <int DT>
+hipError_t launch_patch(const uint32_t* idx, const void* xf, uint32_t n, const float* alpha,
+                        uint32_t vpr, uint32_t n_vec, void* out, bool slow, uint32_t* err,
+                        hipStream_t s);
+
+// Tile encoder (ep_encode.hip) with an option for tables built with escapes: `substitute` codes a
+// field value that its table lacks as the table's substitute (its most probable value, the lowest
+// on ties) instead of reporting an alphabet error.
+ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
+                           uint32_t tile_fields, const ep_tables* h_tables, bool substitute,
+                           void* d_workspace, size_t workspace_bytes, uint32_t* d_word_off,
+                           uint32_t* d_max_tile_words, uint32_t* d_states, uint16_t* d_words,
+                           int64_t words_cap, uint32_t* d_err, hipStream_t s);
+
+// The exception list of quantised vectors under tables built with escapes (ep_encode.hip): every
+// vector with a field its table lacks, in vector order, as idx = v | coset << 31 and its eight
+// fields (16 bytes each).  Uses the encoder workspace and d_scratch (>= 16 bytes per vector) and
+// synchronises `s`.
+ep_status find_exceptions(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
+                          uint32_t tile_fields, const ep_tables* h_tables, void* d_workspace,
+                          size_t workspace_bytes, void* d_scratch, std::vector<uint32_t>& idx,
+                          std::vector<uint8_t>& fields, hipStream_t s);
 
 // Device part of the rate estimate (ep_rate.hip): enqueue on `s` the table build of d_hist and
 // the coded-bit sum of its symbols into the rate workspace (the cost table is copied in when

@@ -480,6 +480,7 @@ static bool valid_dtype(int32_t dt) { return dt >= EP_BF16 && dt <= EP_FP32; }
 
 extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
                                   double* d_out, void* stream) {
+  ep::clear_pending_error();
   if (!d_w || !d_out) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_w) & 15u) return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
@@ -505,6 +506,7 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
                                     const float* d_row_gain, const int64_t* d_row_index,
                                     int64_t n_rows_sel, uint8_t* d_coset, int16_t* d_fields,
                                     ep_hist* d_hist, uint32_t* d_err, void* stream) {
+  ep::clear_pending_error();
   if (!d_w || !d_row_gain || !d_coset || !d_fields || !d_err) return EP_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
@@ -548,6 +550,7 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
 extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, int64_t cols,
                                 const uint8_t* d_coset, const int16_t* d_fields, double* d_num,
                                 int64_t* d_den4, void* stream) {
+  ep::clear_pending_error();
   if (!d_w || !d_coset || !d_fields || !d_num || !d_den4) return EP_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
@@ -573,6 +576,7 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
 
 extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* info,
                                        void* d_dec_tables, void* stream) {
+  ep::clear_pending_error();
   if (!d_blob || !info || !d_dec_tables) return EP_ERR_ARG;
   TableArgs ta;
   for (int t = 0; t < EP_NTABLES; t++) {
@@ -616,6 +620,12 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     if (in.rows < 1 || in.cols < 1 || nv_in >= ((int64_t)1 << 31) || in.tiles < 1 ||
         in.tiles != (nv_in + J * 64 - 1) / (J * 64))
       return EP_ERR_SHAPE;
+    if (in.n_exceptions < 0 || in.n_exceptions > nv_in ||
+        (in.n_exceptions > 0 &&
+         (in.off_exceptions < 64 || (in.off_exceptions & 15) || (in.off_exception_fields & 15) ||
+          in.off_exceptions + 4 * in.n_exceptions > in.off_exception_fields ||
+          in.off_exception_fields + 16 * in.n_exceptions > in.bytes)))
+      return EP_ERR_ARG;
     maxw = std::max(maxw, in.max_tile_words);
     long_rows &= (in.cols + 7) / 8 >= (int64_t)J * 64;   // a tile spans at most two rows
     big |= in.big_alphabet != 0;
@@ -744,6 +754,30 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     const ep_status st = flush(ragged);
     if (st != EP_OK) return st;
   }
+  // escaped vectors, rewritten once the tiles are decoded (stream order)
+  for (int i = 0; i < n; i++) {
+    const ep_blob_info& in = infos[i];
+    if (in.n_exceptions == 0) continue;
+    const uint8_t* p = static_cast<const uint8_t*>(d_blobs[i]);
+    const uint32_t* idx = reinterpret_cast<const uint32_t*>(p + in.off_exceptions);
+    const void* xf = p + in.off_exception_fields;
+    const float* alpha = reinterpret_cast<const float*>(p + in.off_alpha);
+    const uint32_t vpr = (uint32_t)((in.cols + 7) / 8);
+    const uint32_t nvb = (uint32_t)(in.rows * (int64_t)vpr);
+    const uint32_t m = (uint32_t)in.n_exceptions;
+    const bool tiny = in.tiny_scale != 0;
+    hipError_t e;
+    switch (i0.dtype) {
+      case EP_BF16: e = launch_patch<EP_BF16>(idx, xf, m, alpha, vpr, nvb, d_outs[i], tiny, d_err, s); break;
+      case EP_FP16: e = launch_patch<EP_FP16>(idx, xf, m, alpha, vpr, nvb, d_outs[i], false, d_err, s); break;
+      case EP_FP8_E4M3FN:
+        e = launch_patch<EP_FP8_E4M3FN>(idx, xf, m, alpha, vpr, nvb, d_outs[i], false, d_err, s);
+        break;
+      case EP_FP32: e = launch_patch<EP_FP32>(idx, xf, m, alpha, vpr, nvb, d_outs[i], tiny, d_err, s); break;
+      default: e = launch_patch<EP_INT8>(idx, xf, m, alpha, vpr, nvb, d_outs[i], false, d_err, s); break;
+    }
+    if (e != hipSuccess) return EP_ERR_HIP;
+  }
   return EP_OK;
 }
 
@@ -756,6 +790,7 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
 extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* info,
                                       const void* d_dec_tables, void* d_out, uint32_t* d_err,
                                       uint32_t flags, void* stream) {
+  ep::clear_pending_error();
   if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
   return decode_blobs(1, &d_blob, info, &d_dec_tables, &d_out, d_err, flags,
                       static_cast<hipStream_t>(stream));
@@ -765,6 +800,7 @@ extern "C" ep_status ep_decompress_batch(int32_t n, const void* const* d_blobs,
                                          const ep_blob_info* infos,
                                          const void* const* d_dec_tables, void* const* d_outs,
                                          uint32_t* d_err, void* stream) {
+  ep::clear_pending_error();
   return decode_blobs(n, d_blobs, infos, d_dec_tables, d_outs, d_err, 0u,
                       static_cast<hipStream_t>(stream));
 }

@@ -320,6 +320,7 @@ using namespace ep;
 
 extern "C" ep_status ep_build_tables_gpu(const ep_hist* d_hist, ep_tables* d_out, uint32_t* d_err,
                                          void* stream) {
+  ep::clear_pending_error();
   if (!d_hist || !d_out || !d_err) return EP_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   k_build_tables<<<EP_NTABLES, kBT, 0, s>>>(d_hist->counts, d_out, d_err);
@@ -331,6 +332,7 @@ extern "C" size_t ep_estimate_workspace_bytes(void) { return rate_carve(nullptr)
 extern "C" ep_status ep_row_rates(const uint8_t* d_coset, const int16_t* d_fields, int64_t rows,
                                   int64_t cols, const ep_tables* d_tables, const uint32_t* d_cost,
                                   int64_t* d_rates, void* stream) {
+  ep::clear_pending_error();
   if (!d_coset || !d_fields || !d_tables || !d_cost || !d_rates) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
   if (rows < 1 || cols < 1 || rows >= ((int64_t)1 << 31) ||

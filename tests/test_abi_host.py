@@ -241,3 +241,38 @@ def test_encoder_quotient_estimate_bound():
         est = np.floor(q.astype(np.float64)).astype(np.int64)
         worst = max(worst, int(np.abs(est - xr // ff).max()))
     assert worst <= 1
+
+
+def test_blob_parse_exception_list(ep, orc):
+    """The parser reads a version-1.1 blob's exception list where the oracle wrote it, and rejects
+    a list out of order, a vector past the end, and a count the version does not allow."""
+    w = S.student_t_outliers(512, 1024, seed=11, nu=2.0, scale=0.02)
+    st, blob, _ = orc.compress(w, S.FP16, 3.0, 8192, force_s=1.0 / 1000.0)
+    assert st == 0
+    X = orc.blob_exceptions(blob)
+    assert X >= 2
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0 and info.n_exceptions == X
+    o, of = info.off_exceptions, info.off_exception_fields
+    assert o % 16 == 0 and of % 16 == 0 and of + 16 * X == blob.size
+    assert of == o + (4 * X + 15) // 16 * 16
+    nv = info.rows * ((info.cols + 7) // 8)
+    idx = blob[o: o + 4 * X].view(np.uint32)
+    assert np.all(np.diff(idx & 0x7FFFFFFF) > 0) and int(idx[-1] & 0x7FFFFFFF) < nv
+    bad = blob.copy()
+    bi = bad[o: o + 4 * X].view(np.uint32)
+    bi[0], bi[1] = idx[1], idx[0]
+    assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_CORRUPT
+    bad = blob.copy()
+    bad[o + 4 * (X - 1): o + 4 * X].view(np.uint32)[0] = nv
+    assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_CORRUPT
+    bad = blob.copy()
+    bad[5] = 0
+    assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_CORRUPT
+    bad = blob.copy()
+    bad[5] = 2
+    assert ep.ep_blob_parse(bad)[0] == ep.EP_ERR_VERSION
+    # a blob without escapes is version 1.0 with no list
+    st, blob0, _ = orc.compress(S.workload_weights(2, 64, 1024, 0), S.BF16, 4.0, 8192)
+    st, info0 = ep.ep_blob_parse(blob0)
+    assert st == 0 and info0.n_exceptions == 0 and info0.off_exceptions == 0
