@@ -132,3 +132,19 @@ def test_escape_bad_entries(orc):
     keep = np.ones(info.rows, bool)
     keep[r0] = False
     assert np.array_equal(got[keep], ref.view(np.uint16)[keep])
+
+
+@pytest.mark.parametrize("F", [4096, 16384])
+def test_escape_ragged_width(orc, F):
+    """Escapes in a tensor whose width is not a multiple of 8 (zero-padded last vector of each
+    row) and whose last tile is partly filled: the patched vectors land in the padded rows the
+    decoder writes, and the visible columns match the oracle."""
+    w = S.iid_normal(509, 1001, seed=9)
+    s = 1.0 / 1000.0
+    log("escape ragged", F)
+    blob_o, ref = _oracle(orc, w, S.BF16, F, s)
+    assert orc.blob_exceptions(blob_o) > 10000
+    blob, _ = gpu_compress(w, S.BF16, 3.0, F, force_scale=s)
+    assert np.array_equal(blob, blob_o)
+    err, out = GpuBlob(blob).decode()
+    assert err == 0 and np.array_equal(out, ref)
