@@ -260,7 +260,8 @@ double finish_estimate(double acc, const uint32_t* n, int64_t rows, int64_t cols
 
 extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t cols,
                                   int64_t n_sample_rows, uint32_t tile_fields) {
-  if (!h_hist || rows < 1 || cols < 1 || n_sample_rows < 1 || tile_fields < 8) return INFINITY;
+  if (!h_hist || !ep::shape_fits(rows, cols) || n_sample_rows < 1 || tile_fields < 8)
+    return INFINITY;
   std::vector<ep_tables> tv(1);
   ep_tables& T = tv[0];
   if (ep_build_tables(h_hist, EP_PRECISION, &T) != EP_OK) return INFINITY;
@@ -280,7 +281,8 @@ extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64
                                       int64_t n_sample_rows, uint32_t tile_fields,
                                       void* d_workspace, size_t workspace_bytes, void* stream) {
   ep::clear_pending_error();
-  if (!d_hist || !d_workspace || rows < 1 || cols < 1 || n_sample_rows < 1 || tile_fields < 8)
+  if (!d_hist || !d_workspace || !ep::shape_fits(rows, cols) || n_sample_rows < 1 ||
+      tile_fields < 8)
     return INFINITY;
   if (workspace_bytes < ep_estimate_workspace_bytes()) return INFINITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -394,7 +396,7 @@ extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fi
 extern "C" ep_status ep_compress_bound(int64_t rows, int64_t cols, uint32_t tile_fields,
                                        size_t* bytes) {
   if (!bytes) return EP_ERR_ARG;
-  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
+  if (!ep::shape_fits(rows, cols)) return EP_ERR_SHAPE;
   if (tile_fields < 512 || tile_fields % 512) return EP_ERR_ARG;
   const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
   uint32_t nmax[EP_NTABLES];
@@ -469,7 +471,7 @@ inline float row_gain(double sumsq, int64_t cols, double s) {
 }  // namespace
 
 extern "C" size_t ep_compress_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 1) return 0;
+  if (!ep::shape_fits(rows, cols)) return 0;
   return carve(nullptr, rows, cols).total;
 }
 
@@ -500,7 +502,11 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   if (I.rows < 1 || I.cols < 1 || I.tile_fields < 512 || I.tile_fields % 512)
     return EP_ERR_CORRUPT;
   if (I.rows > ((int64_t)1 << 40) || I.cols > ((int64_t)1 << 40)) return EP_ERR_CORRUPT;
-  const int64_t nv = I.rows * ((I.cols + 7) / 8), V = I.tile_fields / 8;
+  // the vector count must stay below 2^31 (the limit of compress and decode); checked before the
+  // product is formed, so a crafted header cannot overflow it
+  const int64_t vpr = (I.cols + 7) / 8;
+  if (I.rows > (((int64_t)1 << 31) - 1) / vpr) return EP_ERR_CORRUPT;
+  const int64_t nv = I.rows * vpr, V = I.tile_fields / 8;
   if (I.tiles != (nv + V - 1) / V) return EP_ERR_CORRUPT;
   if (I.payload_words < 0 || I.payload_words > ((int64_t)1 << 32)) return EP_ERR_CORRUPT;
   uint32_t n_exc;
@@ -600,8 +606,8 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   if (!forced && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
                    cfg->target_bpp <= 11.0))
     return EP_ERR_ARG;
+  if (!ep::shape_fits(rows, cols)) return EP_ERR_SHAPE;
   const int64_t nv = rows * ((cols + 7) / 8);
-  if (nv >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
   if (workspace_bytes < ep_compress_workspace_bytes(rows, cols)) return EP_ERR_CAPACITY;
   const Workspace ws = carve(d_workspace, rows, cols);
   hipStream_t s = static_cast<hipStream_t>(stream);

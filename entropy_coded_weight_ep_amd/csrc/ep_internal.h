@@ -14,6 +14,13 @@ namespace ep {
 // report only its own launches.
 inline void clear_pending_error() { (void)hipGetLastError(); }
 
+// A shape whose vector count rows * ceil(cols / 8) stays below 2^31 (the library's limit),
+// checked without forming the product, so that no caller-supplied size can overflow it.
+inline bool shape_fits(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || cols > ((int64_t)1 << 40)) return false;
+  return rows <= (((int64_t)1 << 31) - 1) / ((cols + 7) / 8);
+}
+
 // Byte offsets (into the blob) and sizes of the 17 table records, for table expansion.
 struct TableArgs {
   int64_t off[EP_NTABLES];

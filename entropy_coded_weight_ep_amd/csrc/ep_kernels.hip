@@ -484,7 +484,7 @@ extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, 
   if (!d_w || !d_out) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_w) & 15u) return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
+  if (!shape_fits(rows, cols)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + 63) / 64));
   const bool pad = cols % 8 != 0;
@@ -511,9 +511,10 @@ extern "C" ep_status ep_quantize_e8(const void* d_w, int32_t dtype, int64_t rows
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
+  if (rows < 1 || cols < 1 || cols > ((int64_t)1 << 40)) return EP_ERR_SHAPE;
   const int64_t nsel = d_row_index ? n_rows_sel : rows;
   if (nsel < 0 || (d_row_index && nsel > (int64_t)1 << 31)) return EP_ERR_ARG;
+  if (nsel > 0 && !shape_fits(nsel, cols)) return EP_ERR_SHAPE;
   const int64_t nvec = nsel * ((cols + 7) / 8);
   if (nvec >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -555,7 +556,7 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
   if ((reinterpret_cast<uintptr_t>(d_w) & 15u) || (reinterpret_cast<uintptr_t>(d_fields) & 15u))
     return EP_ERR_ARG;
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
-  if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
+  if (!shape_fits(rows, cols)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + 63) / 64));
   const bool pad = cols % 8 != 0;
@@ -578,6 +579,7 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
                                        void* d_dec_tables, void* stream) {
   ep::clear_pending_error();
   if (!d_blob || !info || !d_dec_tables) return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_dec_tables) & 15u) return EP_ERR_ARG;
   TableArgs ta;
   for (int t = 0; t < EP_NTABLES; t++) {
     ta.off[t] = info->table_off[t];
@@ -616,8 +618,10 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       return EP_ERR_ARG;
     if (in.precision != EP_PRECISION || in.lanes != EP_LANES) return EP_ERR_VERSION;
     if (in.dtype != i0.dtype || in.tile_fields != i0.tile_fields) return EP_ERR_ARG;
+    // (the vector count is bounded before the product is formed: no overflow on any header)
+    if (!shape_fits(in.rows, in.cols)) return EP_ERR_SHAPE;
     const int64_t nv_in = in.rows * ((in.cols + 7) / 8);
-    if (in.rows < 1 || in.cols < 1 || nv_in >= ((int64_t)1 << 31) || in.tiles < 1 ||
+    if (nv_in >= ((int64_t)1 << 31) || in.tiles < 1 ||
         in.tiles != (nv_in + J * 64 - 1) / (J * 64))
       return EP_ERR_SHAPE;
     if (in.n_exceptions < 0 || in.n_exceptions > nv_in ||

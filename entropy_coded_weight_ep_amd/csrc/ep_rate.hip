@@ -335,9 +335,7 @@ extern "C" ep_status ep_row_rates(const uint8_t* d_coset, const int16_t* d_field
   ep::clear_pending_error();
   if (!d_coset || !d_fields || !d_tables || !d_cost || !d_rates) return EP_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(d_fields) & 15u) return EP_ERR_ARG;
-  if (rows < 1 || cols < 1 || rows >= ((int64_t)1 << 31) ||
-      rows * ((cols + 7) / 8) >= ((int64_t)1 << 31))
-    return EP_ERR_SHAPE;
+  if (!ep::shape_fits(rows, cols)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   k_row_rates<<<(unsigned)rows, kRT, 0, s>>>(d_coset, d_fields, (uint32_t)((cols + 7) / 8), d_tables,
                                              d_cost, d_rates);

@@ -82,6 +82,10 @@ def lib():
             "or_blob_fields": (i32, [P, i64, P, P, P, P, P, P, P, P]),
             "or_estimate_bpp": (dbl, [i32, P, i64, i64, P, i32, dbl]),
             "or_search_scale": (dbl, [i32, P, i64, i64, P, i32, dbl]),
+            "or_estimate_bpp_ex": (dbl, [i32, P, i64, i64, P, i32, i32, i32, dbl]),
+            "or_search_scale_ex": (dbl, [i32, P, i64, i64, P, i32, i32, i32, i32, dbl]),
+            "or_compress_cfg": (i32, [i32, P, i64, i64, P, P, i64, P, P]),
+            "or_config_default": (None, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -289,10 +293,19 @@ def decode_tiles(woff, states, words, nv, tile_fields, lanes, precision, lo, n, 
     return st, cos, fld
 
 
+class OrConfig(C.Structure):
+    """or_config: the oracle's compression settings."""
+    _fields_ = [("target_bpp", C.c_double), ("tile_fields", C.c_int), ("lanes", C.c_int),
+                ("sample_rows", C.c_int), ("search_iters", C.c_int), ("refine", C.c_int),
+                ("force_scale", C.c_double)]
+
+
 def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
-             force_s: float = 0.0, refine: int = 0):
+             force_s: float = 0.0, refine: int = 0, lanes: int = 64, sample_rows: int = 256,
+             search_iters: int = 40):
     """Returns (status, blob bytes as uint8 array, s).  refine: 0, or the odd number (<= 9) of
-    candidate resolutions per row of the rate-distortion refinement."""
+    candidate resolutions per row of the rate-distortion refinement; lanes: rANS states per
+    tile (64 or 128); sample_rows / search_iters: the rate search's sample and bisection steps."""
     w = np.ascontiguousarray(w)
     R, Cc = w.shape
     bound = C.c_int64()
@@ -302,8 +315,10 @@ def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
     blob = np.empty(bound.value, np.uint8)
     nbytes = C.c_int64()
     s = C.c_double()
-    st = lib().or_compress(dtype, _p(w), R, Cc, float(target_bpp), tile_fields, float(force_s),
-                           int(refine), _p(blob), blob.size, C.byref(nbytes), C.byref(s))
+    cfg = OrConfig(float(target_bpp), int(tile_fields), int(lanes), int(sample_rows),
+                   int(search_iters), int(refine), float(force_s))
+    st = lib().or_compress_cfg(dtype, _p(w), R, Cc, C.byref(cfg), _p(blob), blob.size,
+                               C.byref(nbytes), C.byref(s))
     if st:
         return st, None, s.value
     return st, blob[: nbytes.value].copy(), s.value
@@ -333,17 +348,19 @@ def decompress(blob: np.ndarray, t0: int = 0, t1: int = -1, want_fields: bool = 
     return st, out, cos, fld
 
 
-def estimate_bpp(w, dtype, tile_fields, s, sumsq=None):
+def estimate_bpp(w, dtype, tile_fields, s, sumsq=None, lanes: int = 64, sample_rows: int = 256):
     w = np.ascontiguousarray(w)
     ss = row_sumsq(w, dtype) if sumsq is None else sumsq
-    return lib().or_estimate_bpp(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields, s)
+    return lib().or_estimate_bpp_ex(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
+                                    int(lanes), int(sample_rows), s)
 
 
-def search_scale(w, dtype, tile_fields, target_bpp, sumsq=None):
+def search_scale(w, dtype, tile_fields, target_bpp, sumsq=None, lanes: int = 64,
+                 sample_rows: int = 256, search_iters: int = 40):
     w = np.ascontiguousarray(w)
     ss = row_sumsq(w, dtype) if sumsq is None else sumsq
-    return lib().or_search_scale(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
-                                 target_bpp)
+    return lib().or_search_scale_ex(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
+                                    int(lanes), int(sample_rows), int(search_iters), target_bpp)
 
 
 def rate_costs() -> np.ndarray:

@@ -91,6 +91,18 @@ int or_decode_tiles(const uint32_t* word_off, const uint32_t* states, const uint
                     uint8_t* coset, int16_t* fields);
 
 /* blob */
+/* Compression settings (the page's LatticeRANSConfig: target rate, search and refinement
+ * settings).  lanes: rANS states per tile, 64 or 128; sample_rows: rows of the rate search's
+ * sample; search_iters: bisection steps on log2 s; refine: 0 or the odd number (<= 9) of
+ * candidate resolutions per row; force_scale > 0 skips the search. */
+typedef struct {
+  double target_bpp;
+  int tile_fields, lanes, sample_rows, search_iters, refine;
+  double force_scale;
+} or_config;
+void or_config_default(or_config* cfg);
+int or_compress_cfg(int dt, const void* w, int64_t rows, int64_t cols, const or_config* cfg,
+                    uint8_t* blob, int64_t cap, int64_t* out_bytes, double* s_out);
 int or_compress(int dt, const void* w, int64_t rows, int64_t cols, double target_bpp,
                 int tile_fields, double force_s, int refine, uint8_t* blob, int64_t cap,
                 int64_t* out_bytes, double* s_out);
@@ -105,6 +117,11 @@ double or_estimate_bpp(int dt, const void* w, int64_t rows, int64_t cols, const 
                        int tile_fields, double s);
 double or_search_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
                        int tile_fields, double target_bpp);
+double or_estimate_bpp_ex(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
+                          int tile_fields, int lanes, int sample_rows, double s);
+double or_search_scale_ex(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
+                          int tile_fields, int lanes, int sample_rows, int search_iters,
+                          double target_bpp);
 
 /* per-row rate-distortion refinement (refine = number of candidate resolutions, odd, <= 9) */
 void or_rate_costs(uint32_t* cost /* [2^P + 1]: [0] = a value absent from the model */);

@@ -276,3 +276,19 @@ def test_blob_parse_exception_list(ep, orc):
     st, blob0, _ = orc.compress(S.workload_weights(2, 64, 1024, 0), S.BF16, 4.0, 8192)
     st, info0 = ep.ep_blob_parse(blob0)
     assert st == 0 and info0.n_exceptions == 0 and info0.off_exceptions == 0
+
+
+def test_blob_parse_rejects_shapes_that_would_overflow(ep, orc):
+    """Crafted headers whose vector count rows * ceil(cols / 8) is past 2^31 (or past int64) are
+    corrupt; the check runs before the product is formed."""
+    st, blob, _ = orc.compress(S.workload_weights(1), S.BF16, 3.5, 4096)
+    assert ep.ep_blob_parse(blob)[0] == 0
+    for rows, cols in [(1 << 40, 1 << 40), (1 << 31, 8), (1 << 28, 64), ((1 << 31) - 1, 16)]:
+        b = blob.copy()
+        b[8:16] = np.array([rows], np.uint64).view(np.uint8)
+        b[16:24] = np.array([cols], np.uint64).view(np.uint8)
+        assert ep.ep_blob_parse(b)[0] == ep.EP_ERR_CORRUPT, (rows, cols)
+    # entry points that take shapes from the caller refuse them the same way
+    assert ep.ep_compress_workspace_bytes(1 << 40, 1 << 40) == 0
+    with pytest.raises(Exception):
+        ep.ep_compress_bound(1 << 31, 8, 4096)
