@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE = 8
+# rANS states per tile used for each workload unless --lanes says otherwise
+DEFAULT_LANES = {}
 
 
 def main():
@@ -50,6 +52,9 @@ def main():
                     help="override the workload's tile size (4096, 8192 or 16384 fields). "
                          "Smaller tiles give the decoder more independent rANS states to run "
                          "at once, and cost 256 B of states per tile")
+    ap.add_argument("--lanes", type=int, default=0,
+                    help="rANS states per tile: 64 or 128 (two per wavefront lane); 0: the "
+                         "workload's default")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -69,6 +74,7 @@ def main():
     R, C, F, target = wl["rows"], wl["cols"], wl["tile_fields"], wl["target_bpp"]
     if args.tile_fields:
         F = args.tile_fields
+    K = args.lanes or DEFAULT_LANES.get(key, 64)
     dt = wl["dtype"]
     esize = S.ELEM_SIZE[dt]
     tdt = {S.BF16: torch.bfloat16, S.FP16: torch.float16, S.FP8: torch.float8_e4m3fn,
@@ -82,10 +88,10 @@ def main():
     # compress (library: device rate search, quantiser, histogram, LS scales, tables, tile
     # encoder); the second call is the warm time
     t0 = time.time()
-    comp = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F))
+    comp = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F, lanes=K))
     compress_s = time.time() - t0
     t0 = time.time()
-    comp2 = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F))
+    comp2 = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F, lanes=K))
     compress_warm_s = time.time() - t0
     assert np.array_equal(comp.blob, comp2.blob)
     del comp2
@@ -134,7 +140,7 @@ def main():
     if args.refine:
         t0 = time.time()
         rc = ep.compress(t, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F,
-                                                 refine=args.refine))
+                                                 refine=args.refine, lanes=K))
         r_s = time.time() - t0
         r_out = ep.decompress(rc)
         refine = {"candidates": args.refine, "compress_seconds": round(r_s, 3),
@@ -173,12 +179,12 @@ def main():
     T = (nv + F // 8 - 1) // (F // 8)
     d_woff = torch.empty(T + 1, dtype=torch.int32, device=dev)
     d_max = torch.empty(1, dtype=torch.int32, device=dev)
-    d_st = torch.empty(T * 64, dtype=torch.int32, device=dev)
+    d_st = torch.empty(T * K, dtype=torch.int32, device=dev)
     d_words = torch.empty(9 * nv + 1, dtype=torch.int16, device=dev)
 
     def enc():
         assert ep.ep_encode_tiles_gpu(cos, fld, nv, F, h_tab, d_ews, ews, d_woff, d_max, d_st,
-                                      d_words, 9 * nv + 1, qerr) == 0
+                                      d_words, 9 * nv + 1, qerr, lanes=K) == 0
 
     for _ in range(3):
         enc()
@@ -229,7 +235,8 @@ def main():
         for m in range(1, n_mat):
             wm = S.workload_weights(key, index=m)
             tm = torch.from_numpy(wm.view(np.uint8)).to(dev).view(tdt).view(R, C)
-            comps.append(ep.compress(tm, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F)))
+            comps.append(ep.compress(tm, ep.LatticeRANSConfig(target_bpp=target, tile_fields=F,
+                                                              lanes=K)))
             del tm
         bl = [torch.from_numpy(c.blob).to(dev) for c in comps]
         tb = []
@@ -270,7 +277,7 @@ def main():
     algo_bytes = blob_bytes + out_bytes
     achieved = algo_bytes / (ms * 1e-3) / 1e9
     J = F // 512
-    kname = f"k_decode<{J}, {S.DTYPE_NAMES[dt]}>"
+    kname = f"k_decode<{J}, {K // 64}, {S.DTYPE_NAMES[dt]}>"
     line = {
         "metric": "decoded weight GB/s/GPU (output bytes) + % of HBM roofline; actual_bpp",
         "value": round(value, 2),
@@ -285,9 +292,10 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {
-            "workload": wl["name"] + f", target {target} bpp, {F}-field tiles, "
-                        "one fused decode per step",
+            "workload": wl["name"] + f", target {target} bpp, {F}-field tiles, {K} rANS "
+                        "states per tile, one fused decode per step",
             "rows": R, "cols": C, "container": S.DTYPE_NAMES[dt], "tile_fields": F,
+            "lanes": K,
             "target_bpp": target, "actual_bpp": round(info.actual_bpp, 5),
             "scale": comp.scale, "rel_l2": round(rel_l2, 6),
             "blob_bytes": blob_bytes, "output_bytes": out_bytes,
@@ -318,7 +326,7 @@ def main():
     }
     if single is not None:
         line["config"]["workload"] = wl["name"] + f", target {target} bpp, {F}-field tiles, " \
-            f"all {n_mat} matrices decoded by one batched call per step"
+            f"{K} rANS states per tile, all {n_mat} matrices decoded by one batched call per step"
         line["config"].update(single)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(comp.blob, R * C * esize, args.cpu_seconds)

@@ -1,9 +1,10 @@
-// Fused tile decoder instantiated for the int8 container (kernels in ep_decode.h).
+// Fused tile decoder instantiated for the int8 container, one rANS state per lane (64 per tile),
+// and the escape patch launcher (kernels in ep_decode.h).
 #include "ep_decode.h"
 
 namespace ep {
-template hipError_t launch_decode<EP_INT8>(const DecodeArgs&, int, bool, bool, bool, bool, bool,
-                                              int, size_t, hipStream_t);
+template hipError_t launch_decode<EP_INT8, 1>(const DecodeArgs&, int, bool, bool, bool, bool, bool,
+                                          int, size_t, hipStream_t);
 template hipError_t launch_patch<EP_INT8>(const uint32_t*, const void*, uint32_t, const float*,
                                       uint32_t, uint32_t, void*, bool, uint32_t*, hipStream_t);
 }  // namespace ep

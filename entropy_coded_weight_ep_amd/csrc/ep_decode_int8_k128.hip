@@ -1,0 +1,8 @@
+// Fused tile decoder instantiated for the int8 container, two rANS states per lane (128 per
+// tile; kernels in ep_decode.h).
+#include "ep_decode.h"
+
+namespace ep {
+template hipError_t launch_decode<EP_INT8, 2>(const DecodeArgs&, int, bool, bool, bool, bool, bool,
+                                          int, size_t, hipStream_t);
+}  // namespace ep

@@ -8,7 +8,10 @@
 // lanes ascending.  The encoder walks that order backwards, so every tile's stream is the reverse
 // of the words in the order the encoder emits them.
 //
-// One wavefront encodes one tile, lane l owning state l and the vectors l, l+64, ..., l+64(J-1).
+// One wavefront encodes one tile, lane l owning the vectors l, l+64, ..., l+64(J-1).  With 64
+// states per tile lane l holds state l; with 128 (S = 2 per lane) vector l + 64u belongs to state
+// l + 64 (u mod 2), held by the lane as its state u mod 2.  Either way the symbols are visited in
+// the same (phase, u, lane) order, so only the state a step updates changes.
 // At each (phase, vector) step the lanes that must flush a word do so together; in the backward
 // order lane 63 comes first, so a flushing lane's word goes after those of the flushing lanes
 // above it.  The words go onto a per-tile stack in scratch memory in that order, with the tile's
@@ -65,7 +68,7 @@ struct EncOcc {
   static constexpr int waves = J <= 8 ? 8 : (J <= 16 ? (BYTES ? 5 : 4) : (BYTES ? 3 : 2));
 };
 
-template <int J, bool LDS_TAB, bool BYTES>
+template <int J, int S, bool LDS_TAB, bool BYTES>
 __global__ __launch_bounds__(64 * kEncWaves)
 __attribute__((amdgpu_waves_per_eu(EncOcc<J, BYTES>::waves, EncOcc<J, BYTES>::waves)))
 void k_encode_tiles(
@@ -117,7 +120,9 @@ void k_encode_tiles(
     }
   }
 
-  uint32_t x = kL;
+  uint32_t xs[S];
+#pragma unroll
+  for (int i = 0; i < S; i++) xs[i] = kL;
   uint32_t sp = 0;                                  // words emitted so far (wave-uniform)
   uint16_t* const stk = stack + (size_t)t * 9u * V; // room for one word per symbol
 #pragma unroll
@@ -162,6 +167,7 @@ void k_encode_tiles(
       const uint32_t f = use ? fr : 4096u;
       uint32_t cum = use ? e >> 13 : 0u;
       asm volatile("" : "+v"(cum));                 // chosen here: the mask dies before the flush
+      uint32_t& x = xs[j % S];
       const bool flush = (x >> 20) >= f;            // x >= f 2^20
       const uint64_t m = __ballot(flush);
       if (flush) {
@@ -188,7 +194,8 @@ void k_encode_tiles(
     }
   }
   if (__ballot(bad != 0u) != 0ull && lane == 0) atomicOr(err, 1u << EP_ERR_ALPHABET);
-  states[(size_t)t * 64 + lane] = x;
+#pragma unroll
+  for (int i = 0; i < S; i++) states[(size_t)t * 64 * S + 64 * i + lane] = xs[i];
   if (lane == 0) counts[t] = sp;
 }
 
@@ -254,12 +261,16 @@ __global__ __launch_bounds__(256) void k_copy_words(const uint16_t* __restrict__
 }
 
 template <int J, bool LDS_TAB, bool BYTES>
-static void launch_enc(dim3 grid, size_t lds, hipStream_t s, const uint8_t* coset,
+static void launch_enc(dim3 grid, size_t lds, hipStream_t s, int S, const uint8_t* coset,
                        const int16_t* fields, uint32_t nv, uint32_t tiles, const uint32_t* ent,
                        uint32_t n_ent, const EncTabs& ta, uint32_t* counts, uint32_t* states,
                        uint16_t* stack, uint32_t* err) {
-  k_encode_tiles<J, LDS_TAB, BYTES><<<grid, 64 * kEncWaves, lds, s>>>(
-      coset, fields, nv, tiles, ent, n_ent, ta, counts, states, stack, err);
+  if (S == 2)
+    k_encode_tiles<J, 2, LDS_TAB, BYTES><<<grid, 64 * kEncWaves, lds, s>>>(
+        coset, fields, nv, tiles, ent, n_ent, ta, counts, states, stack, err);
+  else
+    k_encode_tiles<J, 1, LDS_TAB, BYTES><<<grid, 64 * kEncWaves, lds, s>>>(
+        coset, fields, nv, tiles, ent, n_ent, ta, counts, states, stack, err);
 }
 
 // Workspace layout: packed table entries, tile counts, per-tile word stacks (9V words each).
@@ -296,7 +307,8 @@ extern "C" size_t ep_encode_workspace_bytes(int64_t n_vectors, uint32_t tile_fie
 namespace ep {
 
 ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
-                           uint32_t tile_fields, const ep_tables* h_tables, bool substitute,
+                           uint32_t tile_fields, uint32_t lanes, const ep_tables* h_tables,
+                           bool substitute,
                            void* d_workspace, size_t workspace_bytes, uint32_t* d_word_off,
                            uint32_t* d_max_tile_words, uint32_t* d_states, uint16_t* d_words,
                            int64_t words_cap, uint32_t* d_err, hipStream_t s) {
@@ -307,6 +319,8 @@ ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int6
   if (n_vectors < 1 || n_vectors >= ((int64_t)1 << 31)) return EP_ERR_SHAPE;
   const int J = (int)(tile_fields / (8 * EP_LANES));
   if (tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_ARG;
+  if (lanes != EP_LANES && lanes != 2 * EP_LANES) return EP_ERR_ARG;
+  const int S = (int)(lanes / EP_LANES);
   if (workspace_bytes < ep_encode_workspace_bytes(n_vectors, tile_fields)) return EP_ERR_CAPACITY;
   const uint32_t nv = (uint32_t)n_vectors;
   const uint32_t V = tile_fields / 8;
@@ -360,11 +374,11 @@ ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int6
   auto go = [&](auto jc, auto lc) {
     if (bytes)
       launch_enc<decltype(jc)::value, decltype(lc)::value, true>(
-          grid, lds, s, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
+          grid, lds, s, S, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
           ws.stack, d_err);
     else
       launch_enc<decltype(jc)::value, decltype(lc)::value, false>(
-          grid, lds, s, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
+          grid, lds, s, S, d_coset, d_fields, nv, tiles, ws.ent, n_ent, ta, ws.counts, d_states,
           ws.stack, d_err);
   };
   using T8 = std::integral_constant<int, 8>;
@@ -509,14 +523,14 @@ ep_status find_exceptions(const uint8_t* d_coset, const int16_t* d_fields, int64
 }  // namespace ep
 
 extern "C" ep_status ep_encode_tiles_gpu(const uint8_t* d_coset, const int16_t* d_fields,
-                                         int64_t n_vectors, uint32_t tile_fields,
+                                         int64_t n_vectors, uint32_t tile_fields, uint32_t lanes,
                                          const ep_tables* h_tables, void* d_workspace,
                                          size_t workspace_bytes, uint32_t* d_word_off,
                                          uint32_t* d_max_tile_words, uint32_t* d_states,
                                          uint16_t* d_words, int64_t words_cap, uint32_t* d_err,
                                          void* stream) {
   ep::clear_pending_error();
-  return ep::encode_tiles_dev(d_coset, d_fields, n_vectors, tile_fields, h_tables, false,
+  return ep::encode_tiles_dev(d_coset, d_fields, n_vectors, tile_fields, lanes, h_tables, false,
                               d_workspace, workspace_bytes, d_word_off, d_max_tile_words,
                               d_states, d_words, words_cap, d_err,
                               static_cast<hipStream_t>(stream));

@@ -23,7 +23,14 @@ namespace {
 
 constexpr uint32_t kM = 1u << EP_PRECISION;
 constexpr uint32_t kL = 1u << 16;
-constexpr int kK = EP_LANES;
+constexpr int kK = EP_LANES;          // states per tile by default
+constexpr int kMaxK = 2 * EP_LANES;   // the most the format allows (two per wavefront lane)
+
+// A lane count the blob format takes for a tile of tile_fields fields: 64 or 128, dividing the
+// tile's vector count.
+inline bool lanes_ok(int64_t lanes, int64_t tile_fields) {
+  return (lanes == kK || lanes == kMaxK) && (tile_fields / 8) % lanes == 0;
+}
 constexpr int kHeaderBytes = 64;
 
 inline int64_t round16(int64_t b) { return (b + 15) / 16 * 16; }
@@ -41,13 +48,14 @@ struct Layout {
 
 // Sections in blob order; a blob with escapes (version 1.1) ends with its exception list: the
 // indices u32[n_exc], then the fields i16[n_exc][8].
-Layout layout(int64_t rows, int64_t tiles, int64_t table_bytes, int64_t words, int64_t n_exc = 0) {
+Layout layout(int64_t rows, int64_t tiles, int64_t lanes, int64_t table_bytes, int64_t words,
+              int64_t n_exc = 0) {
   Layout L;
   L.tables = kHeaderBytes;
   L.alpha = L.tables + table_bytes;
   L.word_off = L.alpha + round16(4 * rows);
   L.states = L.word_off + round16(4 * (tiles + 1));
-  L.words = L.states + round16(4 * (int64_t)kK * tiles);
+  L.words = L.states + round16(4 * lanes * tiles);
   L.exc_idx = L.words + round16(2 * words);
   L.exc_fields = L.exc_idx + round16(4 * n_exc);
   L.total = n_exc > 0 ? L.exc_fields + 16 * n_exc : L.exc_idx;
@@ -114,17 +122,18 @@ std::vector<EncTable> enc_tables(const ep_tables* T) {
   return out;
 }
 
-// Encode one tile into `stream` (forward word order) and its 64 final states.
-bool encode_tile(const uint8_t* cs, const int16_t* fs, int64_t v0, int64_t nvt, int J,
+// Encode one tile into `stream` (forward word order) and its K final states (state k owns the
+// tile's vectors k, k + K, ...; J = vectors per state).
+bool encode_tile(const uint8_t* cs, const int16_t* fs, int64_t v0, int64_t nvt, int J, int K,
                  const std::vector<EncTable>& tabs, uint32_t* states,
                  std::vector<uint16_t>& scratch, std::vector<uint16_t>& stream) {
-  uint32_t x[kK];
-  std::fill(x, x + kK, kL);
+  uint32_t x[kMaxK];
+  std::fill(x, x + K, kL);
   scratch.clear();
   for (int phase = 8; phase >= 0; --phase) {
     for (int j = J - 1; j >= 0; --j) {
-      for (int l = kK - 1; l >= 0; --l) {
-        const int64_t u = l + (int64_t)kK * j;
+      for (int l = K - 1; l >= 0; --l) {
+        const int64_t u = l + (int64_t)K * j;
         if (u >= nvt) continue;
         const int64_t v = v0 + u;
         const int c = cs[v];
@@ -143,7 +152,7 @@ bool encode_tile(const uint8_t* cs, const int16_t* fs, int64_t v0, int64_t nvt, 
     }
   }
   stream.insert(stream.end(), scratch.rbegin(), scratch.rend());
-  std::copy(x, x + kK, states);
+  std::copy(x, x + K, states);
   return true;
 }
 
@@ -181,6 +190,7 @@ extern "C" void ep_config_default(ep_config* cfg) {
   cfg->tile_fields = 8192;
   cfg->sample_rows = 256;
   cfg->search_iters = 40;
+  cfg->lanes = kK;
   cfg->refine = 0;
   cfg->force_scale = 0.0;
 }
@@ -249,18 +259,19 @@ namespace {
 // Bits per element from the sampled symbols' coded size `acc` (bits) and the table sizes:
 // the sample scaled to all rows, plus every byte of the blob before the payload words.
 double finish_estimate(double acc, const uint32_t* n, int64_t rows, int64_t cols,
-                       int64_t n_sample_rows, uint32_t tile_fields) {
+                       int64_t n_sample_rows, uint32_t tile_fields, uint32_t lanes) {
   const double bits = acc * ((double)rows / (double)n_sample_rows);
   const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
-  const Layout L = layout(rows, tiles, tables_bytes(n), 0);
+  const Layout L = layout(rows, tiles, lanes, tables_bytes(n), 0);
   const double meta = (double)L.words;      // everything before the payload words
   return (bits + 8.0 * meta) / ((double)rows * (double)cols);
 }
 }  // namespace
 
 extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t cols,
-                                  int64_t n_sample_rows, uint32_t tile_fields) {
-  if (!h_hist || !ep::shape_fits(rows, cols) || n_sample_rows < 1 || tile_fields < 8)
+                                  int64_t n_sample_rows, uint32_t tile_fields, uint32_t lanes) {
+  if (!h_hist || !ep::shape_fits(rows, cols) || n_sample_rows < 1 || tile_fields < 8 ||
+      !lanes_ok(lanes, tile_fields))
     return INFINITY;
   std::vector<ep_tables> tv(1);
   ep_tables& T = tv[0];
@@ -274,15 +285,15 @@ extern "C" double ep_estimate_bpp(const ep_hist* h_hist, int64_t rows, int64_t c
       acc = acc + (double)c[i] * ((double)EP_PRECISION - std::log2(f));
     }
   }
-  return finish_estimate(acc, T.n, rows, cols, n_sample_rows, tile_fields);
+  return finish_estimate(acc, T.n, rows, cols, n_sample_rows, tile_fields, lanes);
 }
 
 extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64_t cols,
-                                      int64_t n_sample_rows, uint32_t tile_fields,
+                                      int64_t n_sample_rows, uint32_t tile_fields, uint32_t lanes,
                                       void* d_workspace, size_t workspace_bytes, void* stream) {
   ep::clear_pending_error();
   if (!d_hist || !d_workspace || !ep::shape_fits(rows, cols) || n_sample_rows < 1 ||
-      tile_fields < 8)
+      tile_fields < 8 || !lanes_ok(lanes, tile_fields))
     return INFINITY;
   if (workspace_bytes < ep_estimate_workspace_bytes()) return INFINITY;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -292,7 +303,7 @@ extern "C" double ep_estimate_bpp_gpu(const ep_hist* d_hist, int64_t rows, int64
       hipStreamSynchronize(s) != hipSuccess)
     return NAN;
   if (err) return INFINITY;
-  return finish_estimate(bits, n, rows, cols, n_sample_rows, tile_fields);
+  return finish_estimate(bits, n, rows, cols, n_sample_rows, tile_fields, lanes);
 }
 
 extern "C" void ep_rate_costs(uint32_t* h_cost) {
@@ -345,13 +356,15 @@ extern "C" double ep_refine_select(const double* h_D, const int64_t* h_Rq, int64
 }
 
 extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fields,
-                                     int64_t n_vectors, uint32_t tile_fields,
+                                     int64_t n_vectors, uint32_t tile_fields, uint32_t lanes,
                                      const ep_tables* tables, uint32_t* h_word_off,
                                      uint32_t* h_states, uint16_t* h_words, int64_t words_cap) {
   if (!h_coset || !h_fields || !tables || !h_word_off || !h_states || !h_words) return EP_ERR_ARG;
   if (tile_fields < 512 || tile_fields % 512 || n_vectors < 1) return EP_ERR_ARG;
+  if (!lanes_ok(lanes, tile_fields)) return EP_ERR_ARG;
+  const int K = (int)lanes;
   const int64_t V = tile_fields / 8, tiles = (n_vectors + V - 1) / V;
-  const int J = (int)(V / kK);
+  const int J = (int)(V / K);
   const std::vector<EncTable> tabs = enc_tables(tables);
   unsigned nth = std::max(1u, std::thread::hardware_concurrency());
   nth = (unsigned)std::min<int64_t>(nth, tiles);
@@ -366,7 +379,7 @@ extern "C" ep_status ep_encode_tiles(const uint8_t* h_coset, const int16_t* h_fi
     for (int64_t t = t0; t < t1; t++) {
       const size_t before = streams[w].size();
       const int64_t v0 = t * V, nvt = std::min<int64_t>(V, n_vectors - v0);
-      if (!encode_tile(h_coset, h_fields, v0, nvt, J, tabs, h_states + t * kK, scratch,
+      if (!encode_tile(h_coset, h_fields, v0, nvt, J, K, tabs, h_states + t * K, scratch,
                        streams[w])) {
         ok[w] = 0;
         return;
@@ -401,7 +414,7 @@ extern "C" ep_status ep_compress_bound(int64_t rows, int64_t cols, uint32_t tile
   const int64_t nv = rows * ((cols + 7) / 8), V = tile_fields / 8, tiles = (nv + V - 1) / V;
   uint32_t nmax[EP_NTABLES];
   for (int t = 0; t < EP_NTABLES; t++) nmax[t] = 65535;
-  *bytes = (size_t)layout(rows, tiles, tables_bytes(nmax), 9 * nv, nv).total;
+  *bytes = (size_t)layout(rows, tiles, kMaxK, tables_bytes(nmax), 9 * nv, nv).total;
   return EP_OK;
 }
 
@@ -455,7 +468,7 @@ Workspace carve(void* base, int64_t rows, int64_t cols) {
   w.enc = p + o; o += up(w.enc_bytes);
   w.word_off = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (max_tiles + 1));
   w.max_words = reinterpret_cast<uint32_t*>(p + o); o += up(4);
-  w.states = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)kK * max_tiles);
+  w.states = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)kMaxK * max_tiles);
   w.words = reinterpret_cast<uint16_t*>(p + o); o += up(2 * (9 * (size_t)nv + 1));
   w.cost = reinterpret_cast<uint32_t*>(p + o); o += up(4 * (size_t)(kM + 1));
   w.rates = reinterpret_cast<int64_t*>(p + o); o += up(8 * (size_t)rows);
@@ -498,8 +511,9 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   std::memcpy(&u64, b + 48, 8); I.payload_words = (int64_t)u64;
   std::memcpy(&I.max_tile_words, b + 56, 4);
   if (I.dtype < EP_BF16 || I.dtype > EP_FP32) return EP_ERR_DTYPE;
-  if (I.precision != EP_PRECISION || I.lanes != EP_LANES) return EP_ERR_VERSION;
-  if (I.rows < 1 || I.cols < 1 || I.tile_fields < 512 || I.tile_fields % 512)
+  if (I.precision != EP_PRECISION || (I.lanes != kK && I.lanes != kMaxK)) return EP_ERR_VERSION;
+  if (I.rows < 1 || I.cols < 1 || I.tile_fields < 512 || I.tile_fields % 512 ||
+      !lanes_ok(I.lanes, I.tile_fields))
     return EP_ERR_CORRUPT;
   if (I.rows > ((int64_t)1 << 40) || I.cols > ((int64_t)1 << 40)) return EP_ERR_CORRUPT;
   // the vector count must stay below 2^31 (the limit of compress and decode); checked before the
@@ -512,7 +526,7 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   uint32_t n_exc;
   std::memcpy(&n_exc, b + 60, 4);
   if ((b[5] == 0) != (n_exc == 0) || (int64_t)n_exc > nv) return EP_ERR_CORRUPT;
-  const Layout L = layout(I.rows, I.tiles, tb, I.payload_words, n_exc);
+  const Layout L = layout(I.rows, I.tiles, I.lanes, tb, I.payload_words, n_exc);
   if ((int64_t)bytes != L.total) return EP_ERR_CORRUPT;
   // the exception list names vectors in increasing order, each inside the tensor
   for (uint32_t i = 0; i < n_exc; i++) {
@@ -597,6 +611,8 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   if (rows < 1 || cols < 1) return EP_ERR_SHAPE;
   const uint32_t F = cfg->tile_fields;
   if (!device_tile_size(F)) return EP_ERR_ARG;        // the tile sizes the GPU decodes
+  const uint32_t K = cfg->lanes;
+  if (!lanes_ok(K, F)) return EP_ERR_ARG;
   const int nc = (int)cfg->refine;
   if (cfg->refine > 9 || (nc > 0 && nc % 2 == 0)) return EP_ERR_ARG;
   if (nc > 0 && !(std::isfinite(cfg->target_bpp) && cfg->target_bpp >= 0.001 &&
@@ -672,7 +688,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
       hip(hipStreamSynchronize(s));
       if (!hip.ok()) return NAN;
       if (err_host || terr) return INFINITY;
-      return finish_estimate(bits, n, rows, cols, ns, F);
+      return finish_estimate(bits, n, rows, cols, ns, F, K);
     };
     double lo = -20.0, hi = 12.0;
     const double target = cfg->target_bpp;
@@ -755,7 +771,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
       if (err_host & ~(1u << EP_ERR_ALPHABET)) return EP_ERR_ARG;
       if (err_host) break;                            // the model cannot be built: stop here
       const double budget = cfg->target_bpp * (double)rows * (double)cols -
-                            8.0 * (double)layout(rows, tiles, tables_bytes(n_tab), 0).words;
+                            8.0 * (double)layout(rows, tiles, K, tables_bytes(n_tab), 0).words;
       const int64_t budget_q = budget > 0.0 ? std::llround(budget * 65536.0) : 0;
       // the rates of every offered candidate under this model
       for (int k = 0; k < nc; k++) {
@@ -830,7 +846,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   int64_t W;
   {
     hip(hipMemcpyAsync(ws.err, &zero, 4, hipMemcpyHostToDevice, s));
-    if ((st = ep::encode_tiles_dev(ws.coset, ws.fields, nv, F, &T, escapes, ws.enc,
+    if ((st = ep::encode_tiles_dev(ws.coset, ws.fields, nv, F, K, &T, escapes, ws.enc,
                                    ws.enc_bytes, ws.word_off, ws.max_words, ws.states, ws.words,
                                    9 * nv + 1, ws.err, s)) != EP_OK)
       return st;
@@ -840,14 +856,14 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
     if (!hip.ok()) return EP_ERR_HIP;
     if (err_host) return EP_ERR_ARG;
     W = word_off[tiles];
-    L = layout(rows, tiles, tb, W, n_exc);
+    L = layout(rows, tiles, K, tb, W, n_exc);
     *out_bytes = (size_t)L.total;
     if ((size_t)L.total > cap) return EP_ERR_CAPACITY;
     // zero what the copies below do not write: every section before the states (their padding
     // included) and the words section's tail padding; the states fill their section exactly
     std::memset(b, 0, (size_t)L.states);
     std::memset(b + L.words + 2 * W, 0, (size_t)(L.total - L.words - 2 * W));
-    hip(hipMemcpyAsync(b + L.states, ws.states, 4 * kK * tiles, hipMemcpyDeviceToHost, s));
+    hip(hipMemcpyAsync(b + L.states, ws.states, 4 * (size_t)K * tiles, hipMemcpyDeviceToHost, s));
     hip(hipMemcpyAsync(b + L.words, ws.words, 2 * W, hipMemcpyDeviceToHost, s));
     hip(hipStreamSynchronize(s));
     if (!hip.ok()) return EP_ERR_HIP;
@@ -859,7 +875,7 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
   b[6] = (uint8_t)dtype;
   b[7] = EP_PRECISION;
   const uint64_t r64 = (uint64_t)rows, c64 = (uint64_t)cols, w64 = (uint64_t)W;
-  const uint32_t f32 = F, k32 = kK, t32 = (uint32_t)tiles, tb32 = (uint32_t)tb;
+  const uint32_t f32 = F, k32 = K, t32 = (uint32_t)tiles, tb32 = (uint32_t)tb;
   uint32_t maxw = 0;
   for (int64_t t = 0; t < tiles; t++) maxw = std::max(maxw, word_off[t + 1] - word_off[t]);
   std::memcpy(b + 8, &r64, 8);

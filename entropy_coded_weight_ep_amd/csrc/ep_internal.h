@@ -36,14 +36,44 @@ constexpr int kDecWaves = 16;
 constexpr int64_t kCUs = 256;
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
+// The decode tables of one blob (EP_DEC_TABLE_BYTES of device memory), in both forms: the wide-
+// alphabet decoder reads ent + val, the narrow one fent + bias.
+struct DecTables {
+  uint32_t* ent;              // f | (slot - cum) << 13 | (value & 127) << 25: u32[16][4096]
+  int16_t* val;               // value: i16[16][4096]
+  uint32_t* fent;             // f | (value & 255) << 24: u32[16][4096]
+  uint16_t* bias;             // slot - cum: u16[16][4096]
+};
+inline DecTables dec_tables(void* base) {
+  constexpr size_t n = (size_t)16 * (1u << EP_PRECISION);
+  uint8_t* p = static_cast<uint8_t*>(base);
+  DecTables d;
+  d.ent = reinterpret_cast<uint32_t*>(p);
+  d.val = reinterpret_cast<int16_t*>(p + 4 * n);
+  d.fent = reinterpret_cast<uint32_t*>(p + 6 * n);
+  d.bias = reinterpret_cast<uint16_t*>(p + 10 * n);
+  return d;
+}
+
+// LDS byte offsets of the decoder's slot tables (two phase buffers, two cosets).
+// Narrow alphabets: bias tables (u16) at kNarB + 16 KiB b + 8 KiB c, entries (u32) at
+// kNarE + 32 KiB b + 16 KiB c -- each bias at half its entry's address -- up to kNarTop; the waves'
+// regions use [0, kNarB) and [kNarTop, ...).  Wide alphabets: entries from 0, values (i16) from
+// kWideV, up to kWideTop; the waves' regions follow.
+constexpr uint32_t kNarB = 32 * 1024;
+constexpr uint32_t kNarE = 64 * 1024;
+constexpr uint32_t kNarTop = 128 * 1024;
+constexpr uint32_t kWideV = 64 * 1024;
+constexpr uint32_t kWideTop = 96 * 1024;
+
 // One blob's part of the fused tile decoder's arguments.
 struct DecodeBlob {
   const float* alpha;         // f32[rows]
   const uint32_t* word_off;   // u32[tiles + 1]
-  const uint32_t* states;     // u32[tiles][64]
+  const uint32_t* states;     // u32[tiles][K]
   const uint16_t* words;      // u16[payload words], 16-byte aligned section
-  const uint32_t* ent;        // slot entries f | (slot - cum) << 13 | value << 25: u32[16][4096]
-  const int16_t* val;         // field value per slot: i16[16][4096]
+  const uint32_t* ent;        // per-slot u32[16][4096]: wide alphabets DecTables::ent, else fent
+  const uint16_t* val;        // per-slot 16-bit u16[16][4096]: wide DecTables::val, else bias
   void* out;                  // container[rows][cols]
   uint32_t tile_begin, tile_end;  // tiles of this blob decoded by the launch
   uint32_t n_vec, vpr, max_tile_words, coset_f0;
@@ -61,19 +91,21 @@ constexpr int kMaxBatch = 32;
 struct DecodeArgs {
   uint32_t* err;              // device error word
   uint32_t words_stride;      // words per wave region: the largest tile + slack, or the ring size
+  uint32_t low_regions;       // narrow layout: words regions placed below the tables
   uint32_t n;
   uint32_t wg_begin[kMaxBatch + 1];
   DecodeBlob b[kMaxBatch];
 };
 
-// Decoder launchers, one translation unit per container dtype (ep_decode_<dtype>.hip).
+// Decoder launchers, one translation unit per container dtype and states per lane S (K = 64 S per
+// tile): ep_decode_<dtype>.hip (S = 1, with the patch launcher) and ep_decode_<dtype>_k128.hip.
 // `slow`: scale without the fused multiply-add (needed for bf16 when some row scale is tiny).
 // `rows2`: every blob has at least 64 J vectors per row (a tile spans at most two rows), so the
 // kernel keeps two row scales per wave instead of one per vector (used with wide alphabets at
 // J = 32, where it lets 3 waves per SIMD fit the registers).
 // `ring`: stream each tile's words through an LDS ring of words_stride words (a power of two)
 // instead of holding the whole tile.
-template <int DT>
+template <int DT, int S>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
                          bool ring, int waves, size_t lds, hipStream_t s);
 
@@ -84,11 +116,13 @@ hipError_t launch_patch(const uint32_t* idx, const void* xf, uint32_t n, const f
                         uint32_t vpr, uint32_t n_vec, void* out, bool slow, uint32_t* err,
                         hipStream_t s);
 
-// Tile encoder (ep_encode.hip) with an option for tables built with escapes: `substitute` codes a
+// Tile encoder (ep_encode.hip), lanes = 64 or 128 states per tile, with an option for tables built
+// with escapes: `substitute` codes a
 // field value that its table lacks as the table's substitute (its most probable value, the lowest
 // on ties) instead of reporting an alphabet error.
 ep_status encode_tiles_dev(const uint8_t* d_coset, const int16_t* d_fields, int64_t n_vectors,
-                           uint32_t tile_fields, const ep_tables* h_tables, bool substitute,
+                           uint32_t tile_fields, uint32_t lanes, const ep_tables* h_tables,
+                           bool substitute,
                            void* d_workspace, size_t workspace_bytes, uint32_t* d_word_off,
                            uint32_t* d_max_tile_words, uint32_t* d_states, uint16_t* d_words,
                            int64_t words_cap, uint32_t* d_err, hipStream_t s);

@@ -426,22 +426,27 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 
 // ------------------------------------------------------------------------------------------
 // Decode-table expansion (once per blob).  For each of the 16 field tables, slot s of [0, 2^P)
-// belongs to the value v with cum(v) <= s < cum(v) + f(v) and gets
-//   entry = f(v) | (s - cum(v)) << 13 | (v & 127) << 25        (u32)
-//   value = v                                                   (i16, for wide alphabets)
-// The 7-bit value in the entry is exact whenever every field value lies in [-64, 63].
+// belongs to the value v with cum(v) <= s < cum(v) + f(v).  Two forms are written, one for each
+// decoder layout (EP_DEC_TABLE_BYTES holds both, 12 bytes per slot):
+//   wide alphabets:   entry  = f(v) | (s - cum(v)) << 13 | (v & 127) << 25   (u32)
+//                     value  = v                                             (i16)
+//   narrow alphabets: fentry = f(v) | (v & 255) << 24                        (u32; bits 13..23 zero,
+//                                so a 24-bit multiply by fentry multiplies by f)
+//                     bias   = s - cum(v)                                    (u16)
+// The byte of v is exact whenever every field value lies in [-64, 63] (the decoder's narrow case).
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict__ blob,
-                                                       TableArgs ta, uint32_t* __restrict__ ent,
-                                                       int16_t* __restrict__ val) {
+                                                       TableArgs ta, DecTables dt) {
   __shared__ uint32_t scan[256];
   const int t = blockIdx.x;                    // field table 0..15 = blob table 1 + t
   const uint32_t n = ta.n[1 + t];
   const int32_t lo = ta.lo[1 + t];
   const uint16_t* freq = reinterpret_cast<const uint16_t*>(blob + ta.off[1 + t] + 8);
-  uint32_t* E = ent + (size_t)t * kM;
-  int16_t* S = val + (size_t)t * kM;
-  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; }
+  uint32_t* E = dt.ent + (size_t)t * kM;
+  int16_t* S = dt.val + (size_t)t * kM;
+  uint32_t* FE = dt.fent + (size_t)t * kM;
+  uint16_t* B = dt.bias + (size_t)t * kM;
+  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; FE[i] = 0; B[i] = 0; }
   __syncthreads();
   uint32_t base = 0;
   for (uint32_t c0 = 0; c0 < n; c0 += 256) {
@@ -462,6 +467,8 @@ __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict
       if (slot < kM) {
         E[slot] = f | (q << 13) | (((uint32_t)v & 127u) << 25);
         S[slot] = (int16_t)v;
+        FE[slot] = f | (((uint32_t)v & 255u) << 24);
+        B[slot] = (uint16_t)q;
       }
     }
     base += scan[255];
@@ -586,10 +593,8 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
     ta.n[t] = info->n[t];
     ta.lo[t] = info->lo[t];
   }
-  uint32_t* ent = static_cast<uint32_t*>(d_dec_tables);
-  int16_t* val = reinterpret_cast<int16_t*>(ent + 16 * kM);
   k_expand_tables<<<16, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(d_blob), ta, ent, val);
+      static_cast<const uint8_t*>(d_blob), ta, dec_tables(d_dec_tables));
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -606,6 +611,8 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   if (!valid_dtype(i0.dtype)) return EP_ERR_DTYPE;
   const int J = i0.tile_fields / (8 * EP_LANES);
   if (i0.tile_fields % (8 * EP_LANES) || (J != 8 && J != 16 && J != 32)) return EP_ERR_VERSION;
+  if (i0.lanes != EP_LANES && i0.lanes != 2 * EP_LANES) return EP_ERR_VERSION;
+  const int S = i0.lanes / EP_LANES;                 // rANS states per lane
   // batch-wide choices: the largest tile, any wide alphabet, any tiny row scale
   uint32_t maxw = 0;
   bool big = false, slow = false, long_rows = true;
@@ -616,8 +623,10 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     if ((reinterpret_cast<uintptr_t>(d_blobs[i]) & 15u) ||
         (reinterpret_cast<uintptr_t>(d_outs[i]) & 15u))
       return EP_ERR_ARG;
-    if (in.precision != EP_PRECISION || in.lanes != EP_LANES) return EP_ERR_VERSION;
-    if (in.dtype != i0.dtype || in.tile_fields != i0.tile_fields) return EP_ERR_ARG;
+    if (in.precision != EP_PRECISION || (in.lanes != EP_LANES && in.lanes != 2 * EP_LANES))
+      return EP_ERR_VERSION;
+    if (in.dtype != i0.dtype || in.tile_fields != i0.tile_fields || in.lanes != i0.lanes)
+      return EP_ERR_ARG;
     // (the vector count is bounded before the product is formed: no overflow on any header)
     if (!shape_fits(in.rows, in.cols)) return EP_ERR_SHAPE;
     const int64_t nv_in = in.rows * ((in.cols + 7) / 8);
@@ -648,19 +657,27 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
          (uint64_t)ring_stride * 7u < 2ull * maxw)
     ring_stride <<= 1;
   const uint32_t ring_half = (layout == 0 && ring_stride >= 1024u) ? ring_stride / 2 : ring_stride;
-  // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
-  // per wave 256 B of states and the words region.  Waves per workgroup and layout: the choice
-  // that keeps the most tiles resident at once; ties go to the linear layout, then to the smaller
-  // workgroup (spread over more CUs) of at least 4 waves.
-  const size_t lds_tables = (size_t)2 * 2 * kM * 4 + (big ? (size_t)2 * 2 * kM * 2 : 0);
-  auto lds_of = [&](int w, uint32_t stride) {
-    return lds_tables + (size_t)w * (256 + (size_t)stride * 2);
+  // LDS: slot tables (2 phases x 2 cosets x 4096 x 6 B), then per wave 256 S bytes of states
+  // and the words region.  Wide alphabets: the tables take [0, 96 KiB) and the waves' regions
+  // follow.  Narrow alphabets: the tables take [32 KiB, 128 KiB) (the bias tables must sit at
+  // half the entries' addresses); the first words regions go below them, the rest and the states
+  // above.  Waves per workgroup and layout: the choice that keeps the most tiles resident at
+  // once; ties go to the linear layout, then to the smaller workgroup (spread over more CUs) of
+  // at least 4 waves.
+  auto low_of = [&](int w, uint32_t stride) -> uint32_t {
+    return big ? 0u : std::min<uint32_t>((uint32_t)w, kNarB / (stride * 2u));
+  };
+  auto lds_of = [&](int w, uint32_t stride) -> size_t {
+    const size_t rb = (size_t)stride * 2, st = (size_t)256 * S;
+    if (big) return (size_t)kWideTop + (size_t)w * (st + rb);
+    return (size_t)kNarTop + (size_t)(w - low_of(w, stride)) * rb + (size_t)w * st;
   };
   // waves per SIMD the decoder's registers allow: 8, 4 and 4 for 8, 16 and 32 vectors per lane
   // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
-  // tile's vectors twice over and two row scales per wave replace one per vector)
+  // tile's vectors twice over and two row scales per wave replace one per vector; 7 at 8 with
+  // two states per lane and wide alphabets)
   const bool rows2 = J == 32 && big && long_rows;
-  const int occ = J <= 8 ? 8 : (J <= 16 ? 4 : (big ? (rows2 ? 3 : 2) : 4));
+  const int occ = J <= 8 ? ((S == 2 && big) ? 7 : 8) : (J <= 16 ? 4 : (big ? (rows2 ? 3 : 2) : 4));
   const int64_t waves_per_cu = 4 * occ;
   const int max_waves = occ >= 4 ? kDecWaves : (occ == 3 ? 12 : kDecWaves / 2);
   int waves = 0;
@@ -700,18 +717,21 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   DecodeArgs a;
   a.err = d_err;
   a.words_stride = stride;
+  a.low_regions = low_of(waves, stride);
   auto flush = [&](bool ragged) -> ep_status {
     if (a.n == 0) return EP_OK;
     hipError_t e;
+#define EP_LD(DT, SL)                                                                         \
+  (S == 2 ? launch_decode<DT, 2>(a, J, big, ragged, SL, rows2, ring, waves, lds, s)            \
+          : launch_decode<DT, 1>(a, J, big, ragged, SL, rows2, ring, waves, lds, s))
     switch (i0.dtype) {
-      case EP_BF16: e = launch_decode<EP_BF16>(a, J, big, ragged, slow, rows2, ring, waves, lds, s); break;
-      case EP_FP16: e = launch_decode<EP_FP16>(a, J, big, ragged, false, rows2, ring, waves, lds, s); break;
-      case EP_FP8_E4M3FN:
-        e = launch_decode<EP_FP8_E4M3FN>(a, J, big, ragged, false, rows2, ring, waves, lds, s);
-        break;
-      case EP_FP32: e = launch_decode<EP_FP32>(a, J, big, ragged, slow, rows2, ring, waves, lds, s); break;
-      default: e = launch_decode<EP_INT8>(a, J, big, ragged, false, rows2, ring, waves, lds, s); break;
+      case EP_BF16: e = EP_LD(EP_BF16, slow); break;
+      case EP_FP16: e = EP_LD(EP_FP16, false); break;
+      case EP_FP8_E4M3FN: e = EP_LD(EP_FP8_E4M3FN, false); break;
+      case EP_FP32: e = EP_LD(EP_FP32, slow); break;
+      default: e = EP_LD(EP_INT8, false); break;
     }
+#undef EP_LD
     a.n = 0;
     return e == hipSuccess ? EP_OK : EP_ERR_HIP;
   };
@@ -736,8 +756,11 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       b.word_off = reinterpret_cast<const uint32_t*>(p + in.off_word_off);
       b.states = reinterpret_cast<const uint32_t*>(p + in.off_states);
       b.words = reinterpret_cast<const uint16_t*>(p + in.off_words);
-      b.ent = static_cast<const uint32_t*>(d_dec_tables[i]);
-      b.val = reinterpret_cast<const int16_t*>(b.ent + 16 * kM);
+      {
+        const DecTables dt = dec_tables(const_cast<void*>(d_dec_tables[i]));
+        b.ent = big ? dt.ent : dt.fent;                 // the form of the launch's layout
+        b.val = big ? reinterpret_cast<const uint16_t*>(dt.val) : dt.bias;
+      }
       b.out = d_outs[i];
       b.tile_begin = t0;
       b.tile_end = t1;

@@ -127,7 +127,8 @@ class GpuBlob:
 
 
 def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
-                 force_scale: float = 0.0, refine: int = 0):
+                 force_scale: float = 0.0, refine: int = 0, lanes: int = 64,
+                 sample_rows: int = 256, search_iters: int = 40):
     """Library compress of a device copy of w -> (blob bytes, s)."""
     import torch
 
@@ -136,13 +137,14 @@ def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
             5: torch.float32}
     t = dev(w.view(np.uint8)).view(tmap[dtype]).view(w.shape)
     cfg = ep.LatticeRANSConfig(target_bpp=target_bpp, tile_fields=tile_fields,
-                               force_scale=force_scale, refine=refine)
+                               force_scale=force_scale, refine=refine, lanes=lanes,
+                               sample_rows=sample_rows, search_iters=search_iters)
     c = ep.compress(t, cfg)
     return c.blob, c.scale
 
 
 def gpu_encode_tiles(cos: np.ndarray, fld: np.ndarray, tile_fields: int, tables: np.ndarray,
-                     words_cap=None, d_fields_offset_bytes: int = 0):
+                     words_cap=None, d_fields_offset_bytes: int = 0, lanes: int = 64):
     """ep_encode_tiles_gpu on device copies of the symbols -> (status, err word, word_off,
     max_tile_words, states, words[:min(word_off[-1], cap)]).  tables: ep_tables byte layout."""
     import torch
@@ -161,11 +163,11 @@ def gpu_encode_tiles(cos: np.ndarray, fld: np.ndarray, tile_fields: int, tables:
     d_ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     d_woff = torch.full((T + 1,), -1, dtype=torch.int32, device="cuda")
     d_max = torch.zeros(1, dtype=torch.int32, device="cuda")
-    d_states = torch.zeros(max(T, 1) * 64, dtype=torch.int32, device="cuda")
+    d_states = torch.zeros(max(T, 1) * lanes, dtype=torch.int32, device="cuda")
     d_words = torch.zeros(max(cap, 1), dtype=torch.int16, device="cuda")
     d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
     st = ep.ep_encode_tiles_gpu(d_cos, d_fld, nv, tile_fields, tables, d_ws, wsb, d_woff, d_max,
-                                d_states, d_words, cap, d_err)
+                                d_states, d_words, cap, d_err, lanes=lanes)
     torch.cuda.synchronize()
     woff = host(d_woff).view(np.uint32)
     n = min(int(woff[-1]), cap) if st == 0 else 0

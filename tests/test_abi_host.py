@@ -292,3 +292,64 @@ def test_blob_parse_rejects_shapes_that_would_overflow(ep, orc):
     assert ep.ep_compress_workspace_bytes(1 << 40, 1 << 40) == 0
     with pytest.raises(Exception):
         ep.ep_compress_bound(1 << 31, 8, 4096)
+
+
+# ------------------------------------------------------------------------------------------
+# 128 states per tile (two per wavefront lane) and the rate-search settings, on the host
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nv,F", [(512, 4096), (5000, 4096), (100, 8192), (3000, 16384),
+                                  (2048, 8192)])
+def test_encode_tiles_128_lanes_matches_oracle(ep, orc, nv, F):
+    g = np.random.Generator(np.random.PCG64(nv + 7))
+    cos = (g.random(nv) < 0.45).astype(np.uint8)
+    fld = np.rint(g.standard_normal(nv * 8) * 3).astype(np.int16)
+    st, lo, n, freq = orc.build_tables(orc.histogram(cos, fld))
+    st_o, woff_o, states_o, words_o = orc.encode_tiles(cos, fld, F, 128, 12, lo, n, freq)
+    st, woff, states, words = ep.ep_encode_tiles(cos, fld, F, ep.tables_struct(lo, n, freq),
+                                                 lanes=128)
+    assert st == 0 and st_o == 0
+    assert np.array_equal(woff, woff_o)
+    assert np.array_equal(states, states_o)
+    assert np.array_equal(words, words_o)
+
+
+def test_encode_tiles_rejects_other_lane_counts(ep, orc):
+    cos = np.zeros(512, np.uint8)
+    fld = np.zeros(512 * 8, np.int16)
+    st, lo, n, freq = orc.build_tables(orc.histogram(cos, fld))
+    tab = ep.tables_struct(lo, n, freq)
+    for lanes in (32, 96, 256):
+        assert ep.ep_encode_tiles(cos, fld, 4096, tab, lanes=lanes)[0] == ep.EP_ERR_ARG
+    # a tile of 64 vectors cannot hold 128 states' worth of vectors
+    assert ep.ep_encode_tiles(cos, fld, 512, tab, lanes=128)[0] == ep.EP_ERR_ARG
+
+
+@pytest.mark.parametrize("key,shape", [(1, None), (2, (64, 1024)), (3, (64, 512)),
+                                       ("5b", (16, 2048))])
+def test_blob_parse_128_lanes(ep, orc, key, shape):
+    wl = S.WORKLOADS[key]
+    R, Cc = shape or (wl["rows"], wl["cols"])
+    w = S.workload_weights(key, R, Cc)
+    st, blob, s = orc.compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"], lanes=128)
+    assert st == 0
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0 and info.lanes == 128
+    ref = orc.blob_fields(blob)
+    T = ref["tiles"]
+    assert info.off_words - info.off_states == (4 * 128 * T + 15) // 16 * 16
+    assert info.payload_words == ref["payload_words"] and info.bytes == blob.size
+
+
+@pytest.mark.parametrize("lanes", [64, 128])
+@pytest.mark.parametrize("ns", [40, 256, 600])
+def test_estimate_matches_oracle_at_each_setting(ep, orc, lanes, ns):
+    w = S.lognormal_rows(600, 512, seed=4)
+    R, Cc = w.shape
+    s = 0.3
+    sel = (np.arange(min(ns, R)) * R) // min(ns, R)
+    g = orc.gains(orc.row_sumsq(w, S.BF16), Cc, s)
+    st, cos, fld = orc.quantize(w, S.BF16, g, row_sel=sel)
+    assert st == 0
+    est = ep.ep_estimate_bpp(_hist_uint32(orc.histogram(cos, fld)), R, Cc, sel.size, 8192,
+                             lanes=lanes)
+    assert est == orc.estimate_bpp(w, S.BF16, 8192, s, lanes=lanes, sample_rows=ns)
