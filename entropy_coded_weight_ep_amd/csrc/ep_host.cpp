@@ -191,6 +191,7 @@ extern "C" void ep_config_default(ep_config* cfg) {
   cfg->sample_rows = 256;
   cfg->search_iters = 40;
   cfg->lanes = kK;
+  cfg->rate_check = 1;
   cfg->refine = 0;
   cfg->force_scale = 0.0;
 }
@@ -708,6 +709,61 @@ extern "C" ep_status ep_compress(const void* d_w, int32_t dtype, int64_t rows, i
           if (std::isnan(e)) return EP_ERR_HIP;
           if (e <= target) hi = mid;
           else lo = mid;
+        }
+        sc = std::exp2(hi);
+      }
+    }
+    // 2a. whole-tensor check of the searched scale (ep_config.rate_check): the same estimate over
+    // every row; if it misses the target, raise log2 s by 1/8, 1/4, 1/2, ... (to at most 12)
+    // until it meets it, then ten bisection steps keep the meeting end
+    if (cfg->rate_check) {
+      auto full = [&](double e) -> double {
+        const ep_status q = quantise(std::exp2(e), nullptr, rows, {});
+        if (q != EP_OK) return q == EP_ERR_HIP ? NAN : INFINITY;
+        double bits = 0.0;
+        uint32_t terr = 0, n[EP_NTABLES];
+        if (!ep::estimate_enqueue(ws.hist, ws.rate, !cost_sent, s, &bits, &terr, n)) return NAN;
+        cost_sent = true;
+        hip(hipMemcpyAsync(&err_host, ws.err, 4, hipMemcpyDeviceToHost, s));
+        hip(hipStreamSynchronize(s));
+        if (!hip.ok()) return NAN;
+        if (err_host || terr) return INFINITY;
+        return finish_estimate(bits, n, rows, cols, rows, F, K);
+      };
+      double lo = std::log2(sc);
+      double e = full(lo);
+      if (std::isnan(e)) return EP_ERR_HIP;
+      if (e > target) {
+        double hi = lo, step = 0.125;
+        bool met = false;
+        for (;;) {
+          hi = lo + step;
+          if (hi >= 12.0) {
+            hi = 12.0;
+            break;
+          }
+          e = full(hi);
+          if (std::isnan(e)) return EP_ERR_HIP;
+          if (e <= target) {
+            met = true;
+            break;
+          }
+          lo = hi;
+          step *= 2.0;
+        }
+        if (!met) {
+          e = full(hi);
+          if (std::isnan(e)) return EP_ERR_HIP;
+          met = e <= target;
+        }
+        if (met) {
+          for (int it = 0; it < 10; it++) {
+            const double mid = 0.5 * (lo + hi);
+            e = full(mid);
+            if (std::isnan(e)) return EP_ERR_HIP;
+            if (e <= target) hi = mid;
+            else lo = mid;
+          }
         }
         sc = std::exp2(hi);
       }

@@ -36,13 +36,10 @@ constexpr int kDecWaves = 16;
 constexpr int64_t kCUs = 256;
 constexpr int64_t kLdsPerCU = 160 * 1024;
 
-// The decode tables of one blob (EP_DEC_TABLE_BYTES of device memory), in both forms: the wide-
-// alphabet decoder reads ent + val, the narrow one fent + bias.
+// The decode tables of one blob (EP_DEC_TABLE_BYTES of device memory).
 struct DecTables {
   uint32_t* ent;              // f | (slot - cum) << 13 | (value & 127) << 25: u32[16][4096]
-  int16_t* val;               // value: i16[16][4096]
-  uint32_t* fent;             // f | (value & 255) << 24: u32[16][4096]
-  uint16_t* bias;             // slot - cum: u16[16][4096]
+  int16_t* val;               // value: i16[16][4096] (read for wide alphabets)
 };
 inline DecTables dec_tables(void* base) {
   constexpr size_t n = (size_t)16 * (1u << EP_PRECISION);
@@ -50,19 +47,13 @@ inline DecTables dec_tables(void* base) {
   DecTables d;
   d.ent = reinterpret_cast<uint32_t*>(p);
   d.val = reinterpret_cast<int16_t*>(p + 4 * n);
-  d.fent = reinterpret_cast<uint32_t*>(p + 6 * n);
-  d.bias = reinterpret_cast<uint16_t*>(p + 10 * n);
   return d;
 }
 
-// LDS byte offsets of the decoder's slot tables (two phase buffers, two cosets).
-// Narrow alphabets: bias tables (u16) at kNarB + 16 KiB b + 8 KiB c, entries (u32) at
-// kNarE + 32 KiB b + 16 KiB c -- each bias at half its entry's address -- up to kNarTop; the waves'
-// regions use [0, kNarB) and [kNarTop, ...).  Wide alphabets: entries from 0, values (i16) from
-// kWideV, up to kWideTop; the waves' regions follow.
-constexpr uint32_t kNarB = 32 * 1024;
-constexpr uint32_t kNarE = 64 * 1024;
-constexpr uint32_t kNarTop = 128 * 1024;
+// LDS byte offsets of the decoder's slot tables (two phase buffers, two cosets): entries (u32)
+// from 0, and for wide alphabets values (i16) from kWideV; the waves' regions follow the tables,
+// at kNarTop (narrow alphabets) or kWideTop.
+constexpr uint32_t kNarTop = 64 * 1024;
 constexpr uint32_t kWideV = 64 * 1024;
 constexpr uint32_t kWideTop = 96 * 1024;
 
@@ -72,8 +63,8 @@ struct DecodeBlob {
   const uint32_t* word_off;   // u32[tiles + 1]
   const uint32_t* states;     // u32[tiles][K]
   const uint16_t* words;      // u16[payload words], 16-byte aligned section
-  const uint32_t* ent;        // per-slot u32[16][4096]: wide alphabets DecTables::ent, else fent
-  const uint16_t* val;        // per-slot 16-bit u16[16][4096]: wide DecTables::val, else bias
+  const uint32_t* ent;        // slot entries f | (slot - cum) << 13 | value << 25: u32[16][4096]
+  const uint16_t* val;        // field value per slot (bits of an i16): u16[16][4096]
   void* out;                  // container[rows][cols]
   uint32_t tile_begin, tile_end;  // tiles of this blob decoded by the launch
   uint32_t n_vec, vpr, max_tile_words, coset_f0;
@@ -91,7 +82,6 @@ constexpr int kMaxBatch = 32;
 struct DecodeArgs {
   uint32_t* err;              // device error word
   uint32_t words_stride;      // words per wave region: the largest tile + slack, or the ring size
-  uint32_t low_regions;       // narrow layout: words regions placed below the tables
   uint32_t n;
   uint32_t wg_begin[kMaxBatch + 1];
   DecodeBlob b[kMaxBatch];

@@ -426,14 +426,10 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 
 // ------------------------------------------------------------------------------------------
 // Decode-table expansion (once per blob).  For each of the 16 field tables, slot s of [0, 2^P)
-// belongs to the value v with cum(v) <= s < cum(v) + f(v).  Two forms are written, one for each
-// decoder layout (EP_DEC_TABLE_BYTES holds both, 12 bytes per slot):
-//   wide alphabets:   entry  = f(v) | (s - cum(v)) << 13 | (v & 127) << 25   (u32)
-//                     value  = v                                             (i16)
-//   narrow alphabets: fentry = f(v) | (v & 255) << 24                        (u32; bits 13..23 zero,
-//                                so a 24-bit multiply by fentry multiplies by f)
-//                     bias   = s - cum(v)                                    (u16)
-// The byte of v is exact whenever every field value lies in [-64, 63] (the decoder's narrow case).
+// belongs to the value v with cum(v) <= s < cum(v) + f(v) and gets
+//   entry = f(v) | (s - cum(v)) << 13 | (v & 127) << 25        (u32)
+//   value = v                                                   (i16, for wide alphabets)
+// The 7-bit value in the entry is exact whenever every field value lies in [-64, 63].
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict__ blob,
                                                        TableArgs ta, DecTables dt) {
@@ -444,9 +440,7 @@ __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict
   const uint16_t* freq = reinterpret_cast<const uint16_t*>(blob + ta.off[1 + t] + 8);
   uint32_t* E = dt.ent + (size_t)t * kM;
   int16_t* S = dt.val + (size_t)t * kM;
-  uint32_t* FE = dt.fent + (size_t)t * kM;
-  uint16_t* B = dt.bias + (size_t)t * kM;
-  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; FE[i] = 0; B[i] = 0; }
+  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; }
   __syncthreads();
   uint32_t base = 0;
   for (uint32_t c0 = 0; c0 < n; c0 += 256) {
@@ -467,8 +461,6 @@ __global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict
       if (slot < kM) {
         E[slot] = f | (q << 13) | (((uint32_t)v & 127u) << 25);
         S[slot] = (int16_t)v;
-        FE[slot] = f | (((uint32_t)v & 255u) << 24);
-        B[slot] = (uint16_t)q;
       }
     }
     base += scan[255];
@@ -657,20 +649,12 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
          (uint64_t)ring_stride * 7u < 2ull * maxw)
     ring_stride <<= 1;
   const uint32_t ring_half = (layout == 0 && ring_stride >= 1024u) ? ring_stride / 2 : ring_stride;
-  // LDS: slot tables (2 phases x 2 cosets x 4096 x 6 B), then per wave 256 S bytes of states
-  // and the words region.  Wide alphabets: the tables take [0, 96 KiB) and the waves' regions
-  // follow.  Narrow alphabets: the tables take [32 KiB, 128 KiB) (the bias tables must sit at
-  // half the entries' addresses); the first words regions go below them, the rest and the states
-  // above.  Waves per workgroup and layout: the choice that keeps the most tiles resident at
-  // once; ties go to the linear layout, then to the smaller workgroup (spread over more CUs) of
-  // at least 4 waves.
-  auto low_of = [&](int w, uint32_t stride) -> uint32_t {
-    return big ? 0u : std::min<uint32_t>((uint32_t)w, kNarB / (stride * 2u));
-  };
+  // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
+  // per wave 256 S bytes of states and the words region.  Waves per workgroup and layout: the
+  // choice that keeps the most tiles resident at once; ties go to the linear layout, then to the
+  // smaller workgroup (spread over more CUs) of at least 4 waves.
   auto lds_of = [&](int w, uint32_t stride) -> size_t {
-    const size_t rb = (size_t)stride * 2, st = (size_t)256 * S;
-    if (big) return (size_t)kWideTop + (size_t)w * (st + rb);
-    return (size_t)kNarTop + (size_t)(w - low_of(w, stride)) * rb + (size_t)w * st;
+    return (size_t)(big ? kWideTop : kNarTop) + (size_t)w * ((size_t)256 * S + (size_t)stride * 2);
   };
   // waves per SIMD the decoder's registers allow: 8, 4 and 4 for 8, 16 and 32 vectors per lane
   // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
@@ -717,7 +701,6 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   DecodeArgs a;
   a.err = d_err;
   a.words_stride = stride;
-  a.low_regions = low_of(waves, stride);
   auto flush = [&](bool ragged) -> ep_status {
     if (a.n == 0) return EP_OK;
     hipError_t e;
@@ -758,8 +741,8 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       b.words = reinterpret_cast<const uint16_t*>(p + in.off_words);
       {
         const DecTables dt = dec_tables(const_cast<void*>(d_dec_tables[i]));
-        b.ent = big ? dt.ent : dt.fent;                 // the form of the launch's layout
-        b.val = big ? reinterpret_cast<const uint16_t*>(dt.val) : dt.bias;
+        b.ent = dt.ent;
+        b.val = reinterpret_cast<const uint16_t*>(dt.val);
       }
       b.out = d_outs[i];
       b.tile_begin = t0;

@@ -85,6 +85,7 @@ def lib():
             "or_estimate_bpp_ex": (dbl, [i32, P, i64, i64, P, i32, i32, i32, dbl]),
             "or_search_scale_ex": (dbl, [i32, P, i64, i64, P, i32, i32, i32, i32, dbl]),
             "or_compress_cfg": (i32, [i32, P, i64, i64, P, P, i64, P, P]),
+            "or_check_scale": (dbl, [i32, P, i64, i64, P, i32, i32, dbl, dbl]),
             "or_config_default": (None, [P]),
         }
         for name, (res, args) in sig.items():
@@ -297,12 +298,12 @@ class OrConfig(C.Structure):
     """or_config: the oracle's compression settings."""
     _fields_ = [("target_bpp", C.c_double), ("tile_fields", C.c_int), ("lanes", C.c_int),
                 ("sample_rows", C.c_int), ("search_iters", C.c_int), ("refine", C.c_int),
-                ("force_scale", C.c_double)]
+                ("force_scale", C.c_double), ("rate_check", C.c_int)]
 
 
 def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
              force_s: float = 0.0, refine: int = 0, lanes: int = 64, sample_rows: int = 256,
-             search_iters: int = 40):
+             search_iters: int = 40, rate_check: int = 1):
     """Returns (status, blob bytes as uint8 array, s).  refine: 0, or the odd number (<= 9) of
     candidate resolutions per row of the rate-distortion refinement; lanes: rANS states per
     tile (64 or 128); sample_rows / search_iters: the rate search's sample and bisection steps."""
@@ -316,7 +317,7 @@ def compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
     nbytes = C.c_int64()
     s = C.c_double()
     cfg = OrConfig(float(target_bpp), int(tile_fields), int(lanes), int(sample_rows),
-                   int(search_iters), int(refine), float(force_s))
+                   int(search_iters), int(refine), float(force_s), int(rate_check))
     st = lib().or_compress_cfg(dtype, _p(w), R, Cc, C.byref(cfg), _p(blob), blob.size,
                                C.byref(nbytes), C.byref(s))
     if st:
@@ -361,6 +362,13 @@ def search_scale(w, dtype, tile_fields, target_bpp, sumsq=None, lanes: int = 64,
     ss = row_sumsq(w, dtype) if sumsq is None else sumsq
     return lib().or_search_scale_ex(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
                                     int(lanes), int(sample_rows), int(search_iters), target_bpp)
+
+
+def check_scale(w, dtype, tile_fields, target_bpp, s0, sumsq=None, lanes: int = 64):
+    w = np.ascontiguousarray(w)
+    ss = row_sumsq(w, dtype) if sumsq is None else sumsq
+    return lib().or_check_scale(dtype, _p(w), w.shape[0], w.shape[1], _p(ss), tile_fields,
+                                int(lanes), float(target_bpp), float(s0))
 
 
 def rate_costs() -> np.ndarray:

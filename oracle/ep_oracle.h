@@ -94,11 +94,13 @@ int or_decode_tiles(const uint32_t* word_off, const uint32_t* states, const uint
 /* Compression settings (the page's LatticeRANSConfig: target rate, search and refinement
  * settings).  lanes: rANS states per tile, 64 or 128; sample_rows: rows of the rate search's
  * sample; search_iters: bisection steps on log2 s; refine: 0 or the odd number (<= 9) of
- * candidate resolutions per row; force_scale > 0 skips the search. */
+ * candidate resolutions per row; force_scale > 0 skips the search; rate_check: 1 (default)
+ * checks the searched scale against the whole tensor's estimate (or_check_scale). */
 typedef struct {
   double target_bpp;
   int tile_fields, lanes, sample_rows, search_iters, refine;
   double force_scale;
+  int rate_check;
 } or_config;
 void or_config_default(or_config* cfg);
 int or_compress_cfg(int dt, const void* w, int64_t rows, int64_t cols, const or_config* cfg,
@@ -117,6 +119,8 @@ double or_estimate_bpp(int dt, const void* w, int64_t rows, int64_t cols, const 
                        int tile_fields, double s);
 double or_search_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
                        int tile_fields, double target_bpp);
+double or_check_scale(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
+                      int tile_fields, int lanes, double target_bpp, double s0);
 double or_estimate_bpp_ex(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,
                           int tile_fields, int lanes, int sample_rows, double s);
 double or_search_scale_ex(int dt, const void* w, int64_t rows, int64_t cols, const double* sumsq,

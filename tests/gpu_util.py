@@ -128,7 +128,7 @@ class GpuBlob:
 
 def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
                  force_scale: float = 0.0, refine: int = 0, lanes: int = 64,
-                 sample_rows: int = 256, search_iters: int = 40):
+                 sample_rows: int = 256, search_iters: int = 40, rate_check: bool = True):
     """Library compress of a device copy of w -> (blob bytes, s)."""
     import torch
 
@@ -138,7 +138,8 @@ def gpu_compress(w: np.ndarray, dtype: int, target_bpp: float, tile_fields: int,
     t = dev(w.view(np.uint8)).view(tmap[dtype]).view(w.shape)
     cfg = ep.LatticeRANSConfig(target_bpp=target_bpp, tile_fields=tile_fields,
                                force_scale=force_scale, refine=refine, lanes=lanes,
-                               sample_rows=sample_rows, search_iters=search_iters)
+                               sample_rows=sample_rows, search_iters=search_iters,
+                               rate_check=rate_check)
     c = ep.compress(t, cfg)
     return c.blob, c.scale
 

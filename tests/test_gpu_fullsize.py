@@ -56,6 +56,9 @@ def test_full_size_workload(orc, key):
     blob, s = gpu_compress(w, dt, wl["target_bpp"], F)
     assert s == s_o
     assert blob.size == blob_o.size and np.array_equal(blob, blob_o)
+    # the stored rate: at most the target (the whole-tensor check), within 3% of it
+    bpp = 8.0 * blob.size / w.size
+    assert 0.97 * wl["target_bpp"] <= bpp <= wl["target_bpp"], bpp
     del blob, w
     log("gpu decode")
     err, out = GpuBlob(blob_o).decode()

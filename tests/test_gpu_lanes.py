@@ -7,7 +7,8 @@ reconstruction*: rANS in independently decodable tiles); the oracle produces suc
 (lanes=128) and the tests hold the library to them bit for bit: the decode of every workload
 shape (ragged tiles, wide alphabets, all three tile sizes, both word layouts, batches), the device
 tile encoder, and the library's compress, whose blob must equal the oracle's byte for byte.  The
-rate-search settings of *Usage* (sample rows, bisection steps) are checked the same way."""
+rate-search settings of *Usage* (sample rows, bisection steps, the whole-tensor rate check) are
+checked the same way."""
 
 import numpy as np
 import pytest
@@ -192,3 +193,18 @@ def test_high_level_api_with_128_lanes(orc):
     assert np.array_equal(r.view(torch.int16).cpu().numpy().view(np.uint16), ref)
     with pytest.raises(ep.EPError):
         ep.compress(t, ep.LatticeRANSConfig(target_bpp=4.0, tile_fields=8192, lanes=96))
+
+
+@pytest.mark.parametrize("check", [True, False])
+def test_compress_rate_check_matches_oracle(orc, check):
+    """An int8 tensor of heavy-tailed values (the 8192 x 28672 int8 recipe at 1024 x 4096), where
+    the sampled estimate undershoots the tensor's: with the check the library raises the scale on
+    whole-tensor estimates exactly as the oracle does; without it both keep the sampled scale."""
+    log("compress rate check", check)
+    _, _, q = S.laplace_pair(1024, 4096, seed=5)
+    st, blob_o, s_o = orc.compress(q, S.INT8, 6.0, 16384, rate_check=int(check))
+    assert st == 0
+    blob, s = gpu_compress(q, S.INT8, 6.0, 16384, rate_check=check)
+    assert s == s_o and np.array_equal(blob, blob_o)
+    if check:
+        assert 8.0 * blob.size / q.size <= 6.0

@@ -224,7 +224,47 @@ def test_compress_uses_the_sample_setting(orc):
     w = S.workload_weights(2, 600, 256)
     for n in (32, 256, 600):
         s = orc.search_scale(w, S.BF16, 4096, 3.0, sample_rows=n)
-        st, blob, s2 = orc.compress(w, S.BF16, 3.0, 4096, sample_rows=n)
+        st, blob, s2 = orc.compress(w, S.BF16, 3.0, 4096, sample_rows=n, rate_check=0)
         assert st == 0 and s2 == s
+        # with the whole-tensor check: the searched scale, or a coarser one that meets the target
+        st, blob, s3 = orc.compress(w, S.BF16, 3.0, 4096, sample_rows=n)
+        assert st == 0 and s3 == orc.check_scale(w, S.BF16, 4096, 3.0, s) and s3 >= s
     st, _, _ = orc.compress(w, S.BF16, 3.0, 4096, sample_rows=0)
     assert st == orc.ERR_ARG
+
+
+# ------------------------------------------------------------------------------------------
+# The whole-tensor check of the searched scale
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("R,C,target", [(1024, 4096, 6.0), (2048, 2048, 6.0), (600, 2048, 4.5)])
+def test_rate_check_on_heavy_tails(orc, R, C, target):
+    """5b's recipe (int8 absmax of Laplace values) at reduced shapes: the 256-row sample misses
+    rare values, its estimate undershoots the tensor's, and the check raises the scale until the
+    whole-tensor estimate meets the target -- to the bisection's resolution (ten halvings of a
+    step of at least 1/8 in log2 s, so within about 2^-13 of a doubling, a few thousandths of a
+    bit per element) -- and the stored rate lands within 3% below it."""
+    _, _, q = S.laplace_pair(R, C, seed=5)
+    ss = orc.row_sumsq(q, S.INT8)
+    s0 = orc.search_scale(q, S.INT8, 16384, target, sumsq=ss)
+    full0 = orc.estimate_bpp(q, S.INT8, 16384, s0, sumsq=ss, sample_rows=R)
+    assert full0 > target                            # the sample alone overshoots here
+    s = orc.check_scale(q, S.INT8, 16384, target, s0, sumsq=ss)
+    full = orc.estimate_bpp(q, S.INT8, 16384, s, sumsq=ss, sample_rows=R)
+    assert s > s0
+    assert target - 0.01 <= full <= target
+    st, blob, s_c = orc.compress(q, S.INT8, target, 16384)
+    assert st == 0 and s_c == s
+    bpp = 8.0 * blob.size / q.size
+    assert 0.97 * target <= bpp <= target
+
+
+def test_rate_check_keeps_a_scale_that_already_meets_the_target(orc):
+    """With every row sampled the sampled estimate is the whole tensor's: the check changes
+    nothing; likewise on a light-tailed tensor whose sample already reaches the target."""
+    w = S.lognormal_rows(96, 1024, seed=21)
+    s0 = orc.search_scale(w, S.BF16, 8192, 3.0)
+    assert orc.check_scale(w, S.BF16, 8192, 3.0, s0) == s0
+    w = S.workload_weights(2, 1024, 1024)
+    s0 = orc.search_scale(w, S.BF16, 8192, 4.0)
+    if orc.estimate_bpp(w, S.BF16, 8192, s0, sample_rows=1024) <= 4.0:
+        assert orc.check_scale(w, S.BF16, 8192, 4.0, s0) == s0
