@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "ep.h"
@@ -795,6 +796,46 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
                                    const void* d_dec_tables, void* d_out, uint32_t* d_err,
                                    void* stream) {
   return ep_decompress_ex(d_blob, info, d_dec_tables, d_out, d_err, 0u, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// The decode without a caller-supplied table buffer and without any allocation: the expanded
+// decode tables go to a file-scope device array, one per GPU, which lives until the process
+// ends.  In host code `scratch` names only a host-side stand-in: its device address is taken
+// once per device with hipGetSymbolAddress, and only that address is ever passed to a kernel.
+// ------------------------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[EP_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];                   // device address of `scratch`, per device
+
+// The address of this device's `scratch` (looked up on the device's first call), or null.
+void* device_scratch(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" ep_status ep_decompress_noalloc(const void* d_blob, const ep_blob_info* info,
+                                           void* d_out, uint32_t* d_err, void* stream) {
+  ep::clear_pending_error();
+  if (!d_blob || !info || !d_out || !d_err) return EP_ERR_ARG;
+  static_assert(EP_NOALLOC_SCRATCH_BYTES >= EP_DEC_TABLE_BYTES, "one blob's decode tables");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return EP_ERR_HIP;
+  if (dev >= kMaxDevices) return EP_ERR_ARG;
+  void* tables = device_scratch(dev);
+  if (!tables) return EP_ERR_HIP;
+  const ep_status st = ep_prepare_decode(d_blob, info, tables, stream);
+  if (st != EP_OK) return st;
+  const void* const t = tables;
+  return decode_blobs(1, &d_blob, info, &t, &d_out, d_err, 0u, static_cast<hipStream_t>(stream));
 }
 
 extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* info,
