@@ -224,7 +224,35 @@ def main():
         consumer = {"m": args.consumer_m, "gemm_ms": round(g_ms, 4),
                     "gemm_tflops": round(flops / (g_ms * 1e-3) / 1e12, 1),
                     "decode_ms": round(ms, 4),
-                    "decode_over_gemm": round(ms / g_ms, 4)}
+                    "decode_over_gemm": round(ms / g_ms, 4),
+                    "unfused_ms": round(ms + g_ms, 4)}
+        # the decode fused into the product (W never written out), on the same rotated blobs
+        if args.consumer_m <= ep.EP_MM_MAX_M and C <= ep.EP_MM_MAX_COLS:
+            Y = torch.empty((args.consumer_m, R), dtype=torch.float32, device=dev)
+
+            def fused(i):
+                k = i % ROTATE
+                st = ep.ep_decompress_matmul(blobs[k], info, tabs[k], X, args.consumer_m, Y, err)
+                if st:
+                    raise ep.EPError(st, "ep_decompress_matmul")
+
+            for i in range(3):
+                fused(i)
+            torch.cuda.synchronize()
+            ev0.record()
+            for i in range(args.steps):
+                fused(i)
+            ev1.record()
+            torch.cuda.synchronize()
+            f_ms = ev0.elapsed_time(ev1) / args.steps
+            assert int(err.item()) == 0
+            consumer.update({
+                "fused_kernel": f"k_decode<{F // 512}, {K // 64}, {S.DTYPE_NAMES[dt]}> + MFMA "
+                                "product",
+                "fused_ms": round(f_ms, 4),
+                "fused_vs_unfused": round((ms + g_ms) / f_ms, 4),
+                "fused_over_decode": round(f_ms / ms, 4)})
+            del Y
         del X
 
     single = None

@@ -85,6 +85,13 @@ struct DecodeArgs {
   uint32_t n;
   uint32_t wg_begin[kMaxBatch + 1];
   DecodeBlob b[kMaxBatch];
+  // the fused product (ep_decompress_matmul, one blob): Y[m][n] = sum_k X[m][k] W[n][k]
+  const void* mm_x;           // X: mm_m x mm_cols container values, row-major
+  float* mm_y;                // Y: mm_m x mm_rows, row-major
+  uint32_t mm_m, mm_cols, mm_rows;
+  uint32_t mm_kpad;           // columns staged per row (zeros past the last): a multiple of 32
+  uint32_t mm_pitch;          // bytes per staged row in LDS
+  uint32_t mm_groups;         // 16-row groups per workgroup (1 or 2), taken one after the other
 };
 
 // Decoder launchers, one translation unit per container dtype and states per lane S (K = 64 S per
@@ -98,6 +105,11 @@ struct DecodeArgs {
 template <int DT, int S>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
                          bool ring, int waves, size_t lds, hipStream_t s);
+// The decode fused into its product (bf16 and fp16 containers, 8 or 16 vectors per lane): one
+// workgroup per 16 rows of the matrix, `waves` waves.  ep_decode_mm_<dtype>.hip.
+template <int DT, int S>
+hipError_t launch_decode_mm(const DecodeArgs& a, int J, bool big, bool ragged, bool slow,
+                            int waves, size_t lds, hipStream_t s);
 
 // Rewrites a blob's escaped vectors after its tiles are decoded (ep_decode_<dtype>.hip): idx and
 // xf are the exception list on the device (n entries), alpha the blob's row scales.

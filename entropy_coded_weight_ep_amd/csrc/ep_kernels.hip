@@ -799,6 +799,118 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
 }
 
 // ------------------------------------------------------------------------------------------
+// The decode fused into its consumer product: Y = X W^T without W in global memory.  A
+// workgroup takes 16 rows of W, decodes the tiles holding them (one wave per tile, the tile
+// decoder's own code and LDS layout), stages the rows' container values in LDS and multiplies
+// them with MFMA; the waves' shares of the columns are summed in wave order.
+// ------------------------------------------------------------------------------------------
+extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info* info,
+                                          const void* d_dec_tables, const void* d_x, int64_t m,
+                                          float* d_y, uint32_t* d_err, void* stream) {
+  ep::clear_pending_error();
+  if (!d_blob || !info || !d_dec_tables || !d_x || !d_y || !d_err) return EP_ERR_ARG;
+  const ep_blob_info& in = *info;
+  if (!valid_dtype(in.dtype)) return EP_ERR_DTYPE;
+  if (in.dtype != EP_BF16 && in.dtype != EP_FP16) return EP_ERR_DTYPE;
+  if (m < 1 || m > EP_MM_MAX_M) return EP_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_blob) & 15u) || (reinterpret_cast<uintptr_t>(d_x) & 15u) ||
+      (reinterpret_cast<uintptr_t>(d_y) & 3u))
+    return EP_ERR_ARG;
+  if (in.precision != EP_PRECISION || (in.lanes != EP_LANES && in.lanes != 2 * EP_LANES))
+    return EP_ERR_VERSION;
+  const int J = in.tile_fields / (8 * EP_LANES);
+  if (in.tile_fields % (8 * EP_LANES) || (J != 8 && J != 16)) return EP_ERR_SHAPE;
+  if (in.cols < 8 || in.cols % 8 || in.cols > EP_MM_MAX_COLS || !shape_fits(in.rows, in.cols))
+    return EP_ERR_SHAPE;
+  const int64_t vpr = in.cols / 8, nv = in.rows * vpr;
+  const int64_t V = (int64_t)J * 64;
+  if (nv >= ((int64_t)1 << 31) || in.tiles < 1 || in.tiles != (nv + V - 1) / V)
+    return EP_ERR_SHAPE;
+  if (in.n_exceptions != 0) return EP_ERR_VERSION;   // escaped vectors need the patch pass
+  const int S = in.lanes / EP_LANES;
+  // waves per workgroup: the tiles a group of 16 rows can touch (16 vpr vectors from any start
+  // touch at most ceil(16 vpr / V) + 1 tiles; exactly 16 vpr / V when that divides)
+  const int64_t gv = 16 * vpr;
+  const int64_t wpg = gv % V == 0 ? gv / V : (gv + V - 1) / V + 1;
+  const uint32_t kpad = (uint32_t)((in.cols + 31) / 32 * 32);
+  const uint32_t pitch = 2u * kpad + 16u;            // +16 B: the 16 rows fall in distinct banks
+  const bool big = in.big_alphabet != 0;
+  const uint32_t lin_stride = ((in.max_tile_words + 7u + 7u) & ~7u) + 64u;
+  const int64_t groups = (in.rows + 15) / 16;
+  // LDS: the decoder's (tables, then per wave its states and words) while decoding, then the
+  // staged rows (16 x pitch) and the waves' partial products (4 KiB each)
+  auto lds_of = [&](int64_t w) -> size_t {
+    const size_t dec = (size_t)(big ? kWideTop : kNarTop) +
+                       (size_t)w * ((size_t)256 * S + (size_t)lin_stride * 2);
+    return std::max(dec, std::max<size_t>((size_t)16 * pitch, (size_t)w * 4096));
+  };
+  // one or two 16-row groups per workgroup: two when that keeps more tiles decoding at once
+  // (registers allow 16 waves per CU; the LDS decides how many workgroups share one)
+  int64_t ng = 0, best = -1;
+  for (int64_t G = 1; G <= 2; G++) {
+    const int64_t w = G * wpg;
+    if (w > kDecWaves || (int64_t)lds_of(w) > kLdsPerCU) continue;
+    const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w), kDecWaves / w);
+    const int64_t wgs = (groups + G - 1) / G;
+    const int64_t resident = std::min(wgs, kCUs * per_cu) * w;
+    if (resident > best) {
+      best = resident;
+      ng = G;
+    }
+  }
+  if (ng == 0) return EP_ERR_SHAPE;                  // a tile's words do not fit beside the rest
+  const int64_t waves = ng * wpg;
+  const size_t lds = lds_of(waves);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  DecodeArgs a;
+  a.err = d_err;
+  a.words_stride = lin_stride;
+  a.n = 1;
+  a.wg_begin[0] = 0;
+  a.wg_begin[1] = (uint32_t)((groups + ng - 1) / ng);
+  DecodeBlob& b = a.b[0];
+  const uint8_t* p = static_cast<const uint8_t*>(d_blob);
+  b.alpha = reinterpret_cast<const float*>(p + in.off_alpha);
+  b.word_off = reinterpret_cast<const uint32_t*>(p + in.off_word_off);
+  b.states = reinterpret_cast<const uint32_t*>(p + in.off_states);
+  b.words = reinterpret_cast<const uint16_t*>(p + in.off_words);
+  {
+    const DecTables dt = dec_tables(const_cast<void*>(d_dec_tables));
+    b.ent = dt.ent;
+    b.val = reinterpret_cast<const uint16_t*>(dt.val);
+  }
+  b.out = nullptr;
+  b.tile_begin = 0;
+  b.tile_end = (uint32_t)in.tiles;
+  b.n_vec = (uint32_t)nv;
+  b.vpr = (uint32_t)vpr;
+  b.max_tile_words = in.max_tile_words;
+  b.coset_f0 = in.coset_freq0;
+  b.lo0 = in.lo[0];
+  b.inv_vpr_f = 1.0f / (float)b.vpr;
+  b.inv_vpr = 1.0 / (double)b.vpr;
+  a.mm_x = d_x;
+  a.mm_y = d_y;
+  a.mm_m = (uint32_t)m;
+  a.mm_cols = (uint32_t)in.cols;
+  a.mm_rows = (uint32_t)in.rows;
+  a.mm_kpad = kpad;
+  a.mm_pitch = pitch;
+  a.mm_groups = (uint32_t)ng;
+  const bool ragged = (int64_t)in.tiles * V != nv;
+  const bool slow = in.tiny_scale != 0;
+  hipError_t e;
+  if (in.dtype == EP_BF16)
+    e = S == 2 ? launch_decode_mm<EP_BF16, 2>(a, J, big, ragged, slow, (int)waves, lds, s)
+               : launch_decode_mm<EP_BF16, 1>(a, J, big, ragged, slow, (int)waves, lds, s);
+  else
+    e = S == 2 ? launch_decode_mm<EP_FP16, 2>(a, J, big, ragged, false, (int)waves, lds, s)
+               : launch_decode_mm<EP_FP16, 1>(a, J, big, ragged, false, (int)waves, lds, s);
+  return e == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------------
 // The decode without a caller-supplied table buffer and without any allocation: the expanded
 // decode tables go to a file-scope device array, one per GPU, which lives until the process
 // ends.  In host code `scratch` names only a host-side stand-in: its device address is taken

@@ -349,6 +349,20 @@ def decompress(blob: np.ndarray, t0: int = 0, t1: int = -1, want_fields: bool = 
     return st, out, cos, fld
 
 
+def decompress_matmul(blob: np.ndarray, x_bits: np.ndarray):
+    """The decoded tensor inside a product (EntroPack abstract: decoding during inference, for
+    workloads such as Transformer prefill and diffusion denoising), by its plain definition:
+    Y[i][n] = sum_k X[i][k] W[n][k], with W the blob's decode (its container values) and X the
+    container values x_bits [m, cols] of the same container, formed in fp64 by a library product.
+    Returns (status, Y [m, rows] fp64, B [m, rows] = sum_k |X[i][k]| |W[n][k]|): B sizes the
+    rounding error of any fp32 evaluation of the same sums."""
+    st, wb, _, _ = decompress(blob)
+    dt = blob_fields(blob)["dtype"]
+    W = widen(wb, dt).astype(np.float64)
+    X = widen(np.ascontiguousarray(x_bits), dt).astype(np.float64)
+    return st, X @ W.T, np.abs(X) @ np.abs(W).T
+
+
 def estimate_bpp(w, dtype, tile_fields, s, sumsq=None, lanes: int = 64, sample_rows: int = 256):
     w = np.ascontiguousarray(w)
     ss = row_sumsq(w, dtype) if sumsq is None else sumsq
