@@ -55,6 +55,9 @@ def main():
     ap.add_argument("--lanes", type=int, default=0,
                     help="rANS states per tile: 64 or 128 (two per wavefront lane); 0: the "
                          "workload's default")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="also run one traced decode (ep_decompress_traced) and report the median "
+                         "clock cycles per tile of each decoder phase")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -197,6 +200,10 @@ def main():
     e_ms = ev0.elapsed_time(ev1) / qsteps
     assert int(qerr.item()) == 0
     assert int(d_woff[-1].item()) == info.payload_words
+    phases = None
+    if args.phase_stamps:
+        phases = phase_stamps(ep, blobs[0], info, tabs[0], outs[0], err, dev)
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -346,6 +353,7 @@ def main():
         },
         "refine": refine,
         "consumer": consumer,
+        "phases": phases,
         "encode": {
             "kernel": f"k_encode_tiles<{F // 512}> + offset scan + word copy",
             "ms": round(e_ms, 6), "vectors": nv,
@@ -388,6 +396,33 @@ def measured_traffic(kernel: str, workload: str):
     if not rec or rec.get("decoder_source_sha") != decoder_source_sha():
         return None
     return rec["traffic_bytes"]
+
+
+def phase_stamps(ep, d_blob, info, d_tab, d_out, err, dev):
+    """One traced decode: per tile, the shader-clock cycles of each decoder phase (median over the
+    tiles)."""
+    import numpy as np
+    import torch
+
+    T = int(info.tiles)
+    st = torch.zeros(T * ep.EP_TRACE_STAMPS, dtype=torch.int64, device=dev)
+    for _ in range(2):                                  # the second run is the one kept
+        if ep.ep_decompress_traced(d_blob, info, d_tab, d_out, err, st):
+            return {"error": "ep_decompress_traced refused this blob"}
+    torch.cuda.synchronize()
+    a = st.view(T, ep.EP_TRACE_STAMPS).cpu().numpy().astype(np.int64)
+    med = lambda x: float(np.median(x))
+    out = {"tiles": T, "prologue": med(a[:, 1] - a[:, 0]), "coset": med(a[:, 2] - a[:, 1])}
+    prev = a[:, 2]
+    for k in range(8):
+        out[f"barrier{k}"] = med(a[:, 3 + 2 * k] - prev)
+        out[f"phase{k}"] = med(a[:, 4 + 2 * k] - a[:, 3 + 2 * k])
+        prev = a[:, 4 + 2 * k]
+    out["end_check"] = med(a[:, 19] - a[:, 18])
+    out["tile_total"] = med(a[:, 19] - a[:, 0])
+    out["unit"] = "shader clock cycles (s_memtime; the counters of different XCDs are not aligned, "\
+                  "so only differences within a tile are used)"
+    return out
 
 
 def cpu_baseline(blob, out_bytes, min_seconds):

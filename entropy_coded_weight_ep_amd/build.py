@@ -14,7 +14,8 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libep.so")
 UNITS = ["ep_kernels.hip"] + [f"ep_decode_{d}{k}.hip" for d in ("bf16", "fp16", "fp8", "int8", "fp32")
                               for k in ("", "_k128")] + [
-    "ep_decode_mm_bf16.hip", "ep_decode_mm_fp16.hip", "ep_encode.hip", "ep_rate.hip",
+    "ep_decode_mm_bf16.hip", "ep_decode_mm_fp16.hip", "ep_decode_trace.hip", "ep_encode.hip",
+    "ep_rate.hip",
     "ep_host.cpp"]
 SOURCES = [os.path.join(CSRC, u) for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "ep.h")] + [

@@ -92,6 +92,7 @@ struct DecodeArgs {
   uint32_t mm_kpad;           // columns staged per row (zeros past the last): a multiple of 32
   uint32_t mm_pitch;          // bytes per staged row in LDS
   uint32_t mm_groups;         // 16-row groups per workgroup (1 or 2), taken one after the other
+  unsigned long long* stamps; // the traced decode (one blob): per tile, the phase-boundary clocks
 };
 
 // Decoder launchers, one translation unit per container dtype and states per lane S (K = 64 S per
@@ -105,6 +106,11 @@ struct DecodeArgs {
 template <int DT, int S>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
                          bool ring, int waves, size_t lds, hipStream_t s);
+// The traced decode (bf16 and fp8 containers): the same kernel recording each tile's phase
+// boundaries.  ep_decode_trace.hip.
+template <int DT, int S>
+hipError_t launch_decode_trace(const DecodeArgs& a, int J, bool big, bool ragged, int waves,
+                               size_t lds, hipStream_t s);
 // The decode fused into its product (bf16 and fp16 containers, 8 or 16 vectors per lane): one
 // workgroup per 16 rows of the matrix, `waves` waves.  ep_decode_mm_<dtype>.hip.
 template <int DT, int S>

@@ -613,9 +613,16 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
 
 // Decodes n blobs of one container and tile size: the full tiles of all of them in launches of up
 // to kMaxBatch blobs, then the ragged last tiles (if any) the same way.
+// stamps (one blob only): the traced decode, which records each tile's phase boundaries; it
+// takes the linear words layout and the fused scaling, for bf16 and fp8 containers.
 static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_info* infos,
                               const void* const* d_dec_tables, void* const* d_outs,
-                              uint32_t* d_err, uint32_t flags, hipStream_t s) {
+                              uint32_t* d_err, uint32_t flags, hipStream_t s,
+                              unsigned long long* stamps = nullptr) {
+  if (stamps) {
+    if (n != 1 || flags) return EP_ERR_ARG;
+    flags = EP_DECODE_LINEAR;
+  }
   const uint32_t layout = flags & (EP_DECODE_LINEAR | EP_DECODE_RING | EP_DECODE_RING_MIN);
   if ((flags & ~layout) || (layout & (layout - 1u))) return EP_ERR_ARG;
   if (n < 1 || !d_blobs || !infos || !d_dec_tables || !d_outs || !d_err) return EP_ERR_ARG;
@@ -680,7 +687,9 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
   // tile's vectors twice over and two row scales per wave replace one per vector; 7 at 8 with
   // two states per lane and wide alphabets)
-  const bool rows2 = J == 32 && big && long_rows;
+  const bool rows2 = J == 32 && big && long_rows && !stamps;
+  if (stamps && ((i0.dtype != EP_BF16 && i0.dtype != EP_FP8_E4M3FN) || slow))
+    return EP_ERR_VERSION;                           // not instantiated with the trace
   const int occ = J <= 8 ? ((S == 2 && big) ? 7 : 8) : (J <= 16 ? 4 : (big ? (rows2 ? 3 : 2) : 4));
   const int64_t waves_per_cu = 4 * occ;
   const int max_waves = occ >= 4 ? kDecWaves : (occ == 3 ? 12 : kDecWaves / 2);
@@ -721,9 +730,20 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   DecodeArgs a;
   a.err = d_err;
   a.words_stride = stride;
+  a.stamps = stamps;
   auto flush = [&](bool ragged) -> ep_status {
     if (a.n == 0) return EP_OK;
     hipError_t e;
+    if (stamps) {
+      if (i0.dtype == EP_BF16)
+        e = S == 2 ? launch_decode_trace<EP_BF16, 2>(a, J, big, ragged, waves, lds, s)
+                   : launch_decode_trace<EP_BF16, 1>(a, J, big, ragged, waves, lds, s);
+      else
+        e = S == 2 ? launch_decode_trace<EP_FP8_E4M3FN, 2>(a, J, big, ragged, waves, lds, s)
+                   : launch_decode_trace<EP_FP8_E4M3FN, 1>(a, J, big, ragged, waves, lds, s);
+      a.n = 0;
+      return e == hipSuccess ? EP_OK : EP_ERR_HIP;
+    }
 #define EP_LD(DT, SL)                                                                         \
   (S == 2 ? launch_decode<DT, 2>(a, J, big, ragged, SL, rows2, ring, waves, lds, s)            \
           : launch_decode<DT, 1>(a, J, big, ragged, SL, rows2, ring, waves, lds, s))
@@ -885,6 +905,7 @@ extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info
   DecodeArgs a;
   a.err = d_err;
   a.words_stride = lin_stride;
+  a.stamps = nullptr;
   a.n = 1;
   a.wg_begin[0] = 0;
   a.wg_begin[1] = (uint32_t)((groups + ng - 1) / ng);
@@ -976,6 +997,16 @@ extern "C" ep_status ep_decompress_ex(const void* d_blob, const ep_blob_info* in
   if (!d_blob || !info || !d_dec_tables || !d_out || !d_err) return EP_ERR_ARG;
   return decode_blobs(1, &d_blob, info, &d_dec_tables, &d_out, d_err, flags,
                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" ep_status ep_decompress_traced(const void* d_blob, const ep_blob_info* info,
+                                          const void* d_dec_tables, void* d_out, uint32_t* d_err,
+                                          unsigned long long* d_stamps, void* stream) {
+  ep::clear_pending_error();
+  if (!d_blob || !info || !d_dec_tables || !d_out || !d_err || !d_stamps) return EP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(d_stamps) & 7u) return EP_ERR_ARG;
+  return decode_blobs(1, &d_blob, info, &d_dec_tables, &d_out, d_err, 0u,
+                      static_cast<hipStream_t>(stream), d_stamps);
 }
 
 extern "C" ep_status ep_decompress_batch(int32_t n, const void* const* d_blobs,
