@@ -687,7 +687,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
   // tile's vectors twice over and two row scales per wave replace one per vector; 7 at 8 with
   // two states per lane and wide alphabets)
-  const bool rows2 = J == 32 && big && long_rows && !stamps;
+  const bool rows2 = J == 32 && long_rows && !stamps;
   if (stamps && ((i0.dtype != EP_BF16 && i0.dtype != EP_FP8_E4M3FN) || slow))
     return EP_ERR_VERSION;                           // not instantiated with the trace
   const int occ = J <= 8 ? ((S == 2 && big) ? 7 : 8) : (J <= 16 ? 4 : (big ? (rows2 ? 3 : 2) : 4));
