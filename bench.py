@@ -62,8 +62,9 @@ def main():
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decoder shards tiles with no exchange, and no "
-              "multi-GPU run is part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the decoder shards tiles with no exchange, so a GPU's "
+              "throughput is its share's; multi-GPU runs are not measured (use --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
