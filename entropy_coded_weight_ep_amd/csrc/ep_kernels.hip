@@ -679,7 +679,8 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // LDS: slot tables (2 phases x 2 cosets x 4096 x 4 B, + 2 B values for wide alphabets), then
   // per wave 256 S bytes of states and the words region.  Waves per workgroup and layout: the
   // choice that keeps the most tiles resident at once; ties go to the linear layout, then to the
-  // smaller workgroup (spread over more CUs) of at least 4 waves.
+  // less crowded CU (the smaller workgroup, spread over more CUs, unless it would share CUs) of
+  // at least 4 waves.
   auto lds_of = [&](int w, uint32_t stride) -> size_t {
     return (size_t)(big ? kWideTop : kNarTop) + (size_t)w * ((size_t)256 * S + (size_t)stride * 2);
   };
@@ -696,7 +697,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   int waves = 0;
   bool ring = false;
   uint32_t stride = 0;
-  int64_t best = -1;
+  int64_t best = -1, best_crowd = 0;
   // candidates: linear (ties go to it, and among its sizes to the smaller workgroup down to 4
   // waves, below which each wave would load a large share of the tables itself), then the full
   // ring and the half ring, each taken only when it keeps strictly more tiles resident.  The
@@ -715,8 +716,12 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
           std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, st), waves_per_cu / w);
       const int64_t grid = (total_tiles + w - 1) / w;
       const int64_t resident = std::min(std::min(grid, kCUs * per_cu) * w, total_tiles);
-      if (resident > best || (resident == best && !rg && w >= 4)) {
+      // the most waves one CU holds at once: a smaller workgroup that still ends up two to a CU
+      // (its tables then loaded twice there) gains nothing over a larger one alone
+      const int64_t crowd = std::min((grid + kCUs - 1) / kCUs, per_cu) * w;
+      if (resident > best || (resident == best && !rg && w >= 4 && crowd < best_crowd)) {
         best = resident;
+        best_crowd = crowd;
         waves = w;
         ring = rg;
         stride = st;
