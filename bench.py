@@ -230,6 +230,8 @@ def main():
         g_ms = ev0.elapsed_time(ev1) / 10
         flops = 2.0 * args.consumer_m * R * C
         consumer = {"m": args.consumer_m, "gemm_ms": round(g_ms, 4),
+                    "timing": "events around the calls: at small m torch.matmul's host dispatch "
+                              "can outlast its kernel, so unfused_ms is an upper bound there",
                     "gemm_tflops": round(flops / (g_ms * 1e-3) / 1e12, 1),
                     "decode_ms": round(ms, 4),
                     "decode_over_gemm": round(ms / g_ms, 4),
