@@ -444,43 +444,100 @@ __global__ __launch_bounds__(64) void k_row_lsq(const void* __restrict__ w, int6
 // belongs to the value v with cum(v) <= s < cum(v) + f(v) and gets
 //   entry = f(v) | (s - cum(v)) << 13 | (v & 127) << 25        (u32)
 //   value = v                                                   (i16, for wide alphabets)
-// The 7-bit value in the entry is exact whenever every field value lies in [-64, 63].
+// and a slot that no value covers gets 0 in both.  The 7-bit value in the entry is exact
+// whenever every field value lies in [-64, 63].
+// One 1024-lane workgroup per table, in three steps: a scan of the frequencies gives cum(v) and
+// marks slot cum(v) of each value with f(v) > 0 (mark = slot + 1; the value's index and f(v)
+// beside it); a running maximum of the marks hands every slot the first slot of its run; each
+// lane then writes its 4 consecutive slots with one 16-byte and one 8-byte store.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_expand_tables(const uint8_t* __restrict__ blob,
-                                                       TableArgs ta, DecTables dt) {
-  __shared__ uint32_t scan[256];
+constexpr int kExpandThreads = 1024;
+static_assert(kExpandThreads * 4 == kM, "each lane expands 4 slots");
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t expand_op(uint32_t a, uint32_t b) {
+  return MAX ? (a > b ? a : b) : a + b;
+}
+
+// Scan (sum, or maximum when MAX) of one value per lane over the workgroup: returns the
+// exclusive scan at this lane (0 at lane 0) and sets total to the workgroup's.  part: the wave
+// totals; the call opens with a barrier, so consecutive calls may share it.
+template <bool MAX>
+__device__ __forceinline__ uint32_t expand_scan(uint32_t x, uint32_t* part, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc = expand_op<MAX>(inc, y);
+  }
+  uint32_t exc = __shfl_up(inc, 1, 64);
+  if (lane == 0) exc = 0;
+  __syncthreads();
+  if (lane == 63) part[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kExpandThreads / 64; w++) {
+    const uint32_t p = part[w];
+    if (w < wave) before = expand_op<MAX>(before, p);
+    tot = expand_op<MAX>(tot, p);
+  }
+  total = tot;
+  return expand_op<MAX>(before, exc);
+}
+
+__global__ __launch_bounds__(kExpandThreads) void k_expand_tables(const uint8_t* __restrict__ blob,
+                                                                  TableArgs ta, DecTables dt) {
+  __shared__ __align__(16) uint32_t mark[kM];  // slot + 1 where a value's run starts, else 0
+  __shared__ uint32_t info[kM];                // at such a slot: value index | f(v) << 16
+  __shared__ uint32_t part[kExpandThreads / 64];
   const int t = blockIdx.x;                    // field table 0..15 = blob table 1 + t
   const uint32_t n = ta.n[1 + t];
   const int32_t lo = ta.lo[1 + t];
   const uint16_t* freq = reinterpret_cast<const uint16_t*>(blob + ta.off[1 + t] + 8);
-  uint32_t* E = dt.ent + (size_t)t * kM;
-  int16_t* S = dt.val + (size_t)t * kM;
-  for (uint32_t i = threadIdx.x; i < kM; i += 256) { E[i] = 0; S[i] = 0; }
+  reinterpret_cast<uint4*>(mark)[threadIdx.x] = make_uint4(0, 0, 0, 0);
   __syncthreads();
-  uint32_t base = 0;
-  for (uint32_t c0 = 0; c0 < n; c0 += 256) {
-    const uint32_t s = c0 + threadIdx.x;
-    const uint32_t f = (s < n) ? freq[s] : 0u;
-    scan[threadIdx.x] = f;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-      uint32_t add = (threadIdx.x >= (unsigned)d) ? scan[threadIdx.x - d] : 0u;
-      __syncthreads();
-      scan[threadIdx.x] += add;
-      __syncthreads();
+  uint32_t base = 0, total;                    // base: cum of the pass's first value
+  for (uint32_t c0 = 0; c0 < n; c0 += kExpandThreads) {
+    const uint32_t i = c0 + threadIdx.x;
+    const uint32_t f = i < n ? freq[i] : 0u;
+    const uint32_t cum = base + expand_scan<false>(f, part, total);
+    if (f > 0 && cum < (uint32_t)kM) {
+      mark[cum] = cum + 1;
+      info[cum] = i | f << 16;
     }
-    const uint32_t cum = base + scan[threadIdx.x] - f;
-    const int32_t v = lo + (int32_t)s;
-    for (uint32_t q = 0; q < f; q++) {
-      const uint32_t slot = cum + q;
-      if (slot < kM) {
-        E[slot] = f | (q << 13) | (((uint32_t)v & 127u) << 25);
-        S[slot] = (int16_t)v;
+    base += total;
+  }
+  __syncthreads();
+  const uint4 mk = reinterpret_cast<const uint4*>(mark)[threadIdx.x];
+  uint32_t run[4];
+  run[0] = mk.x;
+  run[1] = expand_op<true>(run[0], mk.y);
+  run[2] = expand_op<true>(run[1], mk.z);
+  run[3] = expand_op<true>(run[2], mk.w);
+  const uint32_t before = expand_scan<true>(run[3], part, total);
+  const uint32_t s0 = 4 * threadIdx.x;         // this lane's slots s0 .. s0 + 3
+  uint32_t e[4];
+  uint16_t v[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint32_t m = expand_op<true>(before, run[k]);
+    e[k] = 0;
+    v[k] = 0;
+    if (m > 0) {
+      const uint32_t start = m - 1, inf = info[start], f = inf >> 16, q = s0 + k - start;
+      if (q < f) {
+        const int32_t val = lo + (int32_t)(inf & 0xffffu);
+        e[k] = f | q << 13 | ((uint32_t)val & 127u) << 25;
+        v[k] = (uint16_t)val;
       }
     }
-    base += scan[255];
-    __syncthreads();
   }
+  reinterpret_cast<uint4*>(dt.ent + (size_t)t * kM)[threadIdx.x] =
+      make_uint4(e[0], e[1], e[2], e[3]);
+  reinterpret_cast<uint2*>(dt.val + (size_t)t * kM)[threadIdx.x] =
+      make_uint2(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16);
 }
 
 }  // namespace ep
@@ -605,7 +662,7 @@ extern "C" ep_status ep_prepare_decode(const void* d_blob, const ep_blob_info* i
     ta.n[t] = info->n[t];
     ta.lo[t] = info->lo[t];
   }
-  k_expand_tables<<<16, 256, 0, static_cast<hipStream_t>(stream)>>>(
+  k_expand_tables<<<16, kExpandThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const uint8_t*>(d_blob), ta, dec_tables(d_dec_tables));
   return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
