@@ -226,9 +226,9 @@ __device__ __forceinline__ QIn<DT> q_fetch(const void* __restrict__ w, int64_t r
 // vectors with a grid stride, fetching the next vector's input before quantising the current
 // one.  The histogram is privatised per workgroup in LDS (values [-256, 255] of every table; the
 // rest go straight to the global counts) and merged once at the end; the coset table's two
-// counts are kept per lane.  Few, large workgroups keep the merge short, and each workgroup
-// starts its merge at a different bin so that they do not all hit the same global counters at
-// once.
+// counts are kept per lane and summed per wavefront at the end.  Few, large workgroups keep the
+// merge short, and each workgroup starts its merge at a different bin so that they do not all
+// hit the same global counters at once.
 constexpr int kQThreads = 1024;
 
 template <int DT, bool PAD>
@@ -251,13 +251,25 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
   uint32_t v = blockIdx.x * (uint32_t)kQThreads + threadIdx.x;
   const QPos step = q_pos(stride, vpr, inv_vpr);
   QPos pos = q_pos(v, vpr, inv_vpr);
-  QIn<DT> cur;
-  if (v < n_vec) cur = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, pos, vpr);
+  // The loads of the next vector are issued at the top of an iteration and the stores of the
+  // previous one right after them, so that both complete during this iteration's arithmetic:
+  // while loads and stores are both outstanding the compiler can only wait for all of them at
+  // once, which it does before the next iteration.
+  QIn<DT> nxt;
+  if (v < n_vec) nxt = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, pos, vpr);
+  bool has_prev = false;
+  uint32_t v_prev = 0, c_prev = 0;
+  uint4 pk_prev = uint4{0u, 0u, 0u, 0u};
   for (; v < n_vec; v += stride) {
-    QIn<DT> nxt;
+    const QIn<DT> cur = nxt;                       // fetched one iteration ago
     const bool more = v + stride < n_vec;         // (no overflow: n_vec + stride < 2^32)
     pos = q_advance(pos, step, vpr);               // the position of v + stride
     if (more) nxt = q_fetch<DT, PAD>(w, rows, cols, gain, row_index, pos, vpr);
+    if (has_prev) {
+      coset[v_prev] = (uint8_t)c_prev;
+      reinterpret_cast<uint4*>(fields)[v_prev] = pk_prev;
+    }
+    has_prev = false;
     if (!cur.ok) {                                // a row index outside the tensor: skip, report
       bad_row = true;
     } else {
@@ -296,8 +308,10 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
         c = 0;                                    // left out of the histogram
         pk = uint4{0u, 0u, 0u, 0u};
       }
-      coset[v] = (uint8_t)c;
-      reinterpret_cast<uint4*>(fields)[v] = pk;
+      has_prev = true;                            // written in the next iteration
+      v_prev = v;
+      c_prev = (uint32_t)c;
+      pk_prev = pk;
       if (do_hist && !out_of_range) {
         n_c1 += (uint32_t)c;
         n_c0 += 1u - (uint32_t)c;
@@ -311,7 +325,9 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
                              pk_add16(pk.z, 0x00100010u) | pk_add16(pk.w, 0x00100010u);
         const uint32_t orr = pk_add16(pk.x, 0x01000100u) | pk_add16(pk.y, 0x01000100u) |
                              pk_add16(pk.z, 0x01000100u) | pk_add16(pk.w, 0x01000100u);
-        if ((orn & 0xFFE0FFE0u) == 0u) {          // every field among the hottest values
+        // the hottest-bin copies take a wavefront's vectors only when every one of them fits
+        // there: a mixed wavefront would run both paths, twice the LDS adds
+        if (__ballot((orn & 0xFFE0FFE0u) != 0u) == 0ull) {   // every field among the hottest
           uint32_t* const hn =
               sn + ((threadIdx.x & (kNarrowCopies - 1)) * 16 + 8 * c) * kNarrowStride + kNarrowOff;
 #pragma unroll
@@ -331,13 +347,26 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
         }
       }
     }
-    cur = nxt;
+  }
+  if (has_prev) {
+    coset[v_prev] = (uint8_t)c_prev;
+    reinterpret_cast<uint4*>(fields)[v_prev] = pk_prev;
   }
   if (bad) atomicOr(err, 1u << EP_ERR_RANGE);
   if (bad_row) atomicOr(err, 1u << EP_ERR_ARG);
   if (do_hist) {
-    if (n_c0) atomicAdd(&sh[kHistOff + 0], n_c0);
-    if (n_c1) atomicAdd(&sh[kHistOff + 1], n_c1);
+    // the coset counts summed over the wavefront first: one LDS add per wavefront (the adds of
+    // all 1024 lanes to the same two counters are serialised, and took a quarter of the kernel)
+    uint32_t s0 = n_c0, s1 = n_c1;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      s0 += __shfl_xor(s0, d, 64);
+      s1 += __shfl_xor(s1, d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      if (s0) atomicAdd(&sh[kHistOff + 0], s0);
+      if (s1) atomicAdd(&sh[kHistOff + 1], s1);
+    }
     __syncthreads();
     // fold the copies of the hottest bins into the window (one thread per bin)
     for (int i = threadIdx.x; i < 16 * kNarrowWin; i += kQThreads) {
