@@ -30,52 +30,69 @@ namespace ep {
 
 constexpr uint32_t kNormM = 1u << EP_PRECISION;
 constexpr int kBT = 1024;                          // threads of a table-build workgroup
+static_assert(EP_HIST_BINS % (4 * kBT) == 0, "whole 16-byte loads per thread");
 
-// Largest 64-bit key of a workgroup (every thread passes one; all threads get the result).
-__device__ uint64_t block_max_u64(uint64_t v, uint64_t* s) {
-  s[threadIdx.x] = v;
-  __syncthreads();
-  for (int d = kBT / 2; d > 0; d >>= 1) {
-    if ((int)threadIdx.x < d && s[threadIdx.x + d] > s[threadIdx.x]) s[threadIdx.x] = s[threadIdx.x + d];
-    __syncthreads();
+// Largest (MAX) or total 64-bit value of a workgroup: every thread passes one and all get the
+// result.  Shuffles within each wavefront, then the 16 wavefront results through LDS (s: at
+// least kBT / 64 entries); it ends with a barrier, so s may be reused at once.
+template <bool MAX>
+__device__ uint64_t block_reduce_u64(uint64_t v, uint64_t* s) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = MAX ? (o > v ? o : v) : v + o;
   }
-  const uint64_t r = s[0];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = s[0];
+#pragma unroll
+  for (int w = 1; w < kBT / 64; w++) r = MAX ? (s[w] > r ? s[w] : r) : r + s[w];
   __syncthreads();
   return r;
 }
-
-__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* s) {
-  s[threadIdx.x] = v;
-  __syncthreads();
-  for (int d = kBT / 2; d > 0; d >>= 1) {
-    if ((int)threadIdx.x < d) s[threadIdx.x] += s[threadIdx.x + d];
-    __syncthreads();
-  }
-  const uint64_t r = s[0];
-  __syncthreads();
-  return r;
-}
+__device__ uint64_t block_max_u64(uint64_t v, uint64_t* s) { return block_reduce_u64<true>(v, s); }
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* s) { return block_reduce_u64<false>(v, s); }
 
 // Table t = blockIdx.x of the histogram -> lo[t], n[t], freq[t][0..n) of the device ep_tables.
 __global__ __launch_bounds__(kBT) void k_build_tables(const uint32_t* __restrict__ hist,
                                                      ep_tables* __restrict__ out,
                                                      uint32_t* __restrict__ err) {
-  __shared__ uint64_t s[kBT];
+  __shared__ uint64_t s[kBT / 64];
   const int t = blockIdx.x;
   const uint32_t* c = hist + (size_t)t * EP_HIST_BINS;
   uint16_t* f = out->freq + (size_t)t * EP_HIST_BINS;
 
-  // span, total and number of distinct values
+  // span, total and number of distinct values.  Each thread visits its bins in increasing
+  // order, so the last nonzero one it sees is its largest.  With 16-byte aligned counts all 16
+  // of a thread's 16-byte loads are issued at once.
   uint32_t first = 0xFFFFFFFFu, last = 0, distinct = 0;
   uint64_t total = 0;
-  for (uint32_t b = threadIdx.x; b < EP_HIST_BINS; b += kBT) {
-    const uint32_t v = c[b];
+  auto visit = [&](uint32_t b, uint32_t v) {
     if (v) {
       first = b < first ? b : first;
       last = b;
       total += v;
       distinct++;
     }
+  };
+  if ((reinterpret_cast<uintptr_t>(c) & 15u) == 0) {
+    const uint4* c4 = reinterpret_cast<const uint4*>(c);
+    constexpr int kQ = EP_HIST_BINS / 4 / kBT;
+    uint4 q[kQ];
+#pragma unroll
+    for (int k = 0; k < kQ; k++) q[k] = c4[threadIdx.x + kBT * k];
+#pragma unroll
+    for (int k = 0; k < kQ; k++) {
+      const uint32_t b = 4u * (threadIdx.x + kBT * k);
+      visit(b, q[k].x);
+      visit(b + 1, q[k].y);
+      visit(b + 2, q[k].z);
+      visit(b + 3, q[k].w);
+    }
+  } else {
+    for (uint32_t b = threadIdx.x; b < EP_HIST_BINS; b += kBT) visit(b, c[b]);
   }
   first = 0xFFFFFFFFu - (uint32_t)block_max_u64(0xFFFFFFFFu - first, s);
   last = (uint32_t)block_max_u64(distinct ? last : 0u, s);
