@@ -75,8 +75,8 @@ struct DecodeBlob {
 
 // Kernel arguments of the fused tile decoder: up to kMaxBatch blobs per launch (same container,
 // tile size and LDS layout).  Workgroups [wg_begin[i], wg_begin[i + 1]) decode blob i.
-// 32 descriptors of 96 B keep the arguments near 3.2 KiB, inside the 4 KiB kernel-argument
-// space.  Fewer, larger launches also waste less on each launch's last, partly filled round of
+// 32 descriptors of 96 B (and the fused product's two pointers per blob) keep the arguments
+// near 3.7 KiB, inside the 4 KiB kernel-argument space.  Fewer, larger launches also waste less on each launch's last, partly filled round of
 // tiles (64 matrices of 3072^2: 589 us in four launches, 541 us in two).
 constexpr int kMaxBatch = 32;
 struct DecodeArgs {
@@ -85,15 +85,16 @@ struct DecodeArgs {
   uint32_t n;
   uint32_t wg_begin[kMaxBatch + 1];
   DecodeBlob b[kMaxBatch];
-  // the fused product (ep_decompress_matmul, one blob): Y[m][n] = sum_k X[m][k] W[n][k]
-  const void* mm_x;           // X: mm_m x mm_cols container values, row-major
-  float* mm_y;                // Y: mm_m x mm_rows, row-major
+  // the fused product (ep_decompress_matmul[_batch]): Y[m][n] = sum_k X[m][k] W[n][k] per blob
+  const void* mm_x[kMaxBatch];  // X: mm_m x mm_cols container values, row-major
+  float* mm_y[kMaxBatch];       // Y: mm_m x mm_rows, row-major
   uint32_t mm_m, mm_cols, mm_rows;
   uint32_t mm_kpad;           // columns staged per row (zeros past the last): a multiple of 32
   uint32_t mm_pitch;          // bytes per staged row in LDS
   uint32_t mm_groups;         // 16-row groups per workgroup (1 or 2), taken one after the other
   unsigned long long* stamps; // the traced decode (one blob): per tile, the phase-boundary clocks
 };
+static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments");
 
 // Decoder launchers, one translation unit per container dtype and states per lane S (K = 64 S per
 // tile): ep_decode_<dtype>.hip (S = 1, with the patch launcher) and ep_decode_<dtype>_k128.hip.

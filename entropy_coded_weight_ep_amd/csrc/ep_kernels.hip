@@ -934,18 +934,17 @@ extern "C" ep_status ep_decompress(const void* d_blob, const ep_blob_info* info,
 // decoder's own code and LDS layout), stages the rows' container values in LDS and multiplies
 // them with MFMA; the waves' shares of the columns are summed in wave order.
 // ------------------------------------------------------------------------------------------
-extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info* info,
-                                          const void* d_dec_tables, const void* d_x, int64_t m,
-                                          float* d_y, uint32_t* d_err, void* stream) {
-  ep::clear_pending_error();
-  if (!d_blob || !info || !d_dec_tables || !d_x || !d_y || !d_err) return EP_ERR_ARG;
-  const ep_blob_info& in = *info;
+// The decode fused into its product for n blobs of one shape (n = 1: ep_decompress_matmul), in
+// launches of up to kMaxBatch blobs: workgroups [wg_begin[i], wg_begin[i + 1]) take blob i's
+// 16-row groups.
+static ep_status matmul_blobs(int n, const void* const* d_blobs, const ep_blob_info* infos,
+                              const void* const* d_tabs, const void* const* d_xs, int64_t m,
+                              float* const* d_ys, uint32_t* d_err, hipStream_t s) {
+  if (n < 1 || !d_blobs || !infos || !d_tabs || !d_xs || !d_ys || !d_err) return EP_ERR_ARG;
+  const ep_blob_info& in = infos[0];
   if (!valid_dtype(in.dtype)) return EP_ERR_DTYPE;
   if (in.dtype != EP_BF16 && in.dtype != EP_FP16) return EP_ERR_DTYPE;
   if (m < 1 || m > EP_MM_MAX_M) return EP_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(d_blob) & 15u) || (reinterpret_cast<uintptr_t>(d_x) & 15u) ||
-      (reinterpret_cast<uintptr_t>(d_y) & 3u))
-    return EP_ERR_ARG;
   if (in.precision != EP_PRECISION || (in.lanes != EP_LANES && in.lanes != 2 * EP_LANES))
     return EP_ERR_VERSION;
   const int J = in.tile_fields / (8 * EP_LANES);
@@ -954,9 +953,25 @@ extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info
     return EP_ERR_SHAPE;
   const int64_t vpr = in.cols / 8, nv = in.rows * vpr;
   const int64_t V = (int64_t)J * 64;
-  if (nv >= ((int64_t)1 << 31) || in.tiles < 1 || in.tiles != (nv + V - 1) / V)
-    return EP_ERR_SHAPE;
-  if (in.n_exceptions != 0) return EP_ERR_VERSION;   // escaped vectors need the patch pass
+  bool big = false, slow = false;
+  uint32_t max_words = 0;
+  for (int i = 0; i < n; i++) {
+    const ep_blob_info& bi = infos[i];
+    if (!d_blobs[i] || !d_tabs[i] || !d_xs[i] || !d_ys[i]) return EP_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_blobs[i]) & 15u) ||
+        (reinterpret_cast<uintptr_t>(d_xs[i]) & 15u) || (reinterpret_cast<uintptr_t>(d_ys[i]) & 3u))
+      return EP_ERR_ARG;
+    if (i > 0 && (bi.dtype != in.dtype || bi.rows != in.rows || bi.cols != in.cols ||
+                  bi.tile_fields != in.tile_fields || bi.lanes != in.lanes ||
+                  bi.precision != in.precision))
+      return EP_ERR_ARG;                             // one shape per call
+    if (bi.tiles < 1 || bi.tiles != (nv + V - 1) / V || nv >= ((int64_t)1 << 31))
+      return EP_ERR_SHAPE;
+    if (bi.n_exceptions != 0) return EP_ERR_VERSION; // escaped vectors need the patch pass
+    big |= bi.big_alphabet != 0;
+    slow |= bi.tiny_scale != 0;
+    max_words = std::max(max_words, bi.max_tile_words);
+  }
   const int S = in.lanes / EP_LANES;
   // waves per workgroup: the tiles a group of 16 rows can touch (16 vpr vectors from any start
   // touch at most ceil(16 vpr / V) + 1 tiles; exactly 16 vpr / V when that divides)
@@ -964,8 +979,7 @@ extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info
   const int64_t wpg = gv % V == 0 ? gv / V : (gv + V - 1) / V + 1;
   const uint32_t kpad = (uint32_t)((in.cols + 31) / 32 * 32);
   const uint32_t pitch = 2u * kpad + 16u;            // +16 B: the 16 rows fall in distinct banks
-  const bool big = in.big_alphabet != 0;
-  const uint32_t lin_stride = ((in.max_tile_words + 7u + 7u) & ~7u) + 64u;
+  const uint32_t lin_stride = ((max_words + 7u + 7u) & ~7u) + 64u;
   const int64_t groups = (in.rows + 15) / 16;
   // LDS: the decoder's (tables, then per wave its states and words) while decoding, then the
   // staged rows (16 x pitch) and the waves' partial products (4 KiB each)
@@ -974,71 +988,96 @@ extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info
                        (size_t)w * ((size_t)256 * S + (size_t)lin_stride * 2);
     return std::max(dec, std::max<size_t>((size_t)16 * pitch, (size_t)w * 4096));
   };
-  // one or two 16-row groups per workgroup: two when that keeps more tiles decoding at once
-  // (registers allow 16 waves per CU; the LDS decides how many workgroups share one)
-  int64_t ng = 0, best = -1;
-  for (int64_t G = 1; G <= 2; G++) {
-    const int64_t w = G * wpg;
-    if (w > kDecWaves || (int64_t)lds_of(w) > kLdsPerCU) continue;
-    const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w), kDecWaves / w);
-    const int64_t wgs = (groups + G - 1) / G;
-    const int64_t resident = std::min(wgs, kCUs * per_cu) * w;
-    if (resident > best) {
-      best = resident;
-      ng = G;
-    }
-  }
-  if (ng == 0) return EP_ERR_SHAPE;                  // a tile's words do not fit beside the rest
-  const int64_t waves = ng * wpg;
-  const size_t lds = lds_of(waves);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  DecodeArgs a;
-  a.err = d_err;
-  a.words_stride = lin_stride;
-  a.stamps = nullptr;
-  a.n = 1;
-  a.wg_begin[0] = 0;
-  a.wg_begin[1] = (uint32_t)((groups + ng - 1) / ng);
-  DecodeBlob& b = a.b[0];
-  const uint8_t* p = static_cast<const uint8_t*>(d_blob);
-  b.alpha = reinterpret_cast<const float*>(p + in.off_alpha);
-  b.word_off = reinterpret_cast<const uint32_t*>(p + in.off_word_off);
-  b.states = reinterpret_cast<const uint32_t*>(p + in.off_states);
-  b.words = reinterpret_cast<const uint16_t*>(p + in.off_words);
-  {
-    const DecTables dt = dec_tables(const_cast<void*>(d_dec_tables));
-    b.ent = dt.ent;
-    b.val = reinterpret_cast<const uint16_t*>(dt.val);
-  }
-  b.out = nullptr;
-  b.tile_begin = 0;
-  b.tile_end = (uint32_t)in.tiles;
-  b.n_vec = (uint32_t)nv;
-  b.vpr = (uint32_t)vpr;
-  b.max_tile_words = in.max_tile_words;
-  b.coset_f0 = in.coset_freq0;
-  b.lo0 = in.lo[0];
-  b.inv_vpr_f = 1.0f / (float)b.vpr;
-  b.inv_vpr = 1.0 / (double)b.vpr;
-  a.mm_x = d_x;
-  a.mm_y = d_y;
-  a.mm_m = (uint32_t)m;
-  a.mm_cols = (uint32_t)in.cols;
-  a.mm_rows = (uint32_t)in.rows;
-  a.mm_kpad = kpad;
-  a.mm_pitch = pitch;
-  a.mm_groups = (uint32_t)ng;
   const bool ragged = (int64_t)in.tiles * V != nv;
-  const bool slow = in.tiny_scale != 0;
-  hipError_t e;
-  if (in.dtype == EP_BF16)
-    e = S == 2 ? launch_decode_mm<EP_BF16, 2>(a, J, big, ragged, slow, (int)waves, lds, s)
-               : launch_decode_mm<EP_BF16, 1>(a, J, big, ragged, slow, (int)waves, lds, s);
-  else
-    e = S == 2 ? launch_decode_mm<EP_FP16, 2>(a, J, big, ragged, false, (int)waves, lds, s)
-               : launch_decode_mm<EP_FP16, 1>(a, J, big, ragged, false, (int)waves, lds, s);
-  return e == hipSuccess ? EP_OK : EP_ERR_HIP;
+  for (int c0 = 0; c0 < n; c0 += kMaxBatch) {
+    const int nb = std::min(n - c0, kMaxBatch);
+    // one or two 16-row groups per workgroup: two when that keeps more tiles decoding at once
+    // (registers allow 16 waves per CU; the LDS decides how many workgroups share one)
+    int64_t ng = 0, best = -1;
+    for (int64_t G = 1; G <= 2; G++) {
+      const int64_t w = G * wpg;
+      if (w > kDecWaves || (int64_t)lds_of(w) > kLdsPerCU) continue;
+      const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w), kDecWaves / w);
+      const int64_t wgs = nb * ((groups + G - 1) / G);
+      const int64_t resident = std::min(wgs, kCUs * per_cu) * w;
+      if (resident > best) {
+        best = resident;
+        ng = G;
+      }
+    }
+    if (ng == 0) return EP_ERR_SHAPE;                // a tile's words do not fit beside the rest
+    const int64_t waves = ng * wpg;
+    const size_t lds = lds_of(waves);
+    DecodeArgs a;
+    a.err = d_err;
+    a.words_stride = lin_stride;
+    a.stamps = nullptr;
+    a.n = (uint32_t)nb;
+    a.wg_begin[0] = 0;
+    for (int i = 0; i < nb; i++) {
+      const ep_blob_info& bi = infos[c0 + i];
+      a.wg_begin[i + 1] = a.wg_begin[i] + (uint32_t)((groups + ng - 1) / ng);
+      DecodeBlob& b = a.b[i];
+      const uint8_t* p = static_cast<const uint8_t*>(d_blobs[c0 + i]);
+      b.alpha = reinterpret_cast<const float*>(p + bi.off_alpha);
+      b.word_off = reinterpret_cast<const uint32_t*>(p + bi.off_word_off);
+      b.states = reinterpret_cast<const uint32_t*>(p + bi.off_states);
+      b.words = reinterpret_cast<const uint16_t*>(p + bi.off_words);
+      {
+        const DecTables dt = dec_tables(const_cast<void*>(d_tabs[c0 + i]));
+        b.ent = dt.ent;
+        b.val = reinterpret_cast<const uint16_t*>(dt.val);
+      }
+      b.out = nullptr;
+      b.tile_begin = 0;
+      b.tile_end = (uint32_t)bi.tiles;
+      b.n_vec = (uint32_t)nv;
+      b.vpr = (uint32_t)vpr;
+      b.max_tile_words = bi.max_tile_words;
+      b.coset_f0 = bi.coset_freq0;
+      b.lo0 = bi.lo[0];
+      b.inv_vpr_f = 1.0f / (float)b.vpr;
+      b.inv_vpr = 1.0 / (double)b.vpr;
+      a.mm_x[i] = d_xs[c0 + i];
+      a.mm_y[i] = d_ys[c0 + i];
+    }
+    a.mm_m = (uint32_t)m;
+    a.mm_cols = (uint32_t)in.cols;
+    a.mm_rows = (uint32_t)in.rows;
+    a.mm_kpad = kpad;
+    a.mm_pitch = pitch;
+    a.mm_groups = (uint32_t)ng;
+    hipError_t e;
+    if (in.dtype == EP_BF16)
+      e = S == 2 ? launch_decode_mm<EP_BF16, 2>(a, J, big, ragged, slow, (int)waves, lds, s)
+                 : launch_decode_mm<EP_BF16, 1>(a, J, big, ragged, slow, (int)waves, lds, s);
+    else
+      e = S == 2 ? launch_decode_mm<EP_FP16, 2>(a, J, big, ragged, false, (int)waves, lds, s)
+                 : launch_decode_mm<EP_FP16, 1>(a, J, big, ragged, false, (int)waves, lds, s);
+    if (e != hipSuccess) return EP_ERR_HIP;
+  }
+  return EP_OK;
+}
+
+extern "C" ep_status ep_decompress_matmul(const void* d_blob, const ep_blob_info* info,
+                                          const void* d_dec_tables, const void* d_x, int64_t m,
+                                          float* d_y, uint32_t* d_err, void* stream) {
+  ep::clear_pending_error();
+  if (!d_blob || !info || !d_dec_tables || !d_x || !d_y || !d_err) return EP_ERR_ARG;
+  return matmul_blobs(1, &d_blob, info, &d_dec_tables, &d_x, m, &d_y, d_err,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" ep_status ep_decompress_matmul_batch(int32_t n, const void* const* d_blobs,
+                                                const ep_blob_info* infos,
+                                                const void* const* d_dec_tables,
+                                                const void* const* d_x, int64_t m,
+                                                float* const* d_y, uint32_t* d_err,
+                                                void* stream) {
+  ep::clear_pending_error();
+  if (n < 1 || n > (1 << 20)) return EP_ERR_ARG;
+  return matmul_blobs(n, d_blobs, infos, d_dec_tables, d_x, m, d_y, d_err,
+                      static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------------------------------

@@ -182,3 +182,114 @@ def test_high_level_decompress_matmul(orc):
     _check(orc, c.blob, xbits, host(y).astype(np.float64))
     with pytest.raises(ep.EPError):
         ep.decompress_matmul(c, x.float())
+
+
+# ---- ep_decompress_matmul_batch: many blobs of one shape in one call ----------------------
+
+def _weights(key, R, C, i):
+    if key == 4:
+        return S.workload_weights(4, R, C, index=i)
+    if key == 3:
+        return S.student_t_outliers(R, C, seed=60 + i)
+    return S.lognormal_rows(R, C, seed=50 + i)
+
+
+def _batch_run(gbs, xs, m, expect_err=0):
+    import torch
+
+    ep = ep_mod()
+    d_xs = [dev(x.view(np.uint16)) for x in xs]
+    d_ys = [torch.full((m, gb.info.rows), float("nan"), dtype=torch.float32, device="cuda")
+            for gb in gbs]
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = ep.ep_decompress_matmul_batch([g.d_blob for g in gbs], [g.info for g in gbs],
+                                       [g.d_tab for g in gbs], d_xs, m, d_ys, d_err)
+    assert st == 0, st
+    torch.cuda.synchronize()
+    assert int(host(d_err)[0]) == expect_err
+    return [host(y).astype(np.float64) for y in d_ys]
+
+
+BATCH_CASES = [
+    # (workload, rows, cols, m, blobs, lanes)
+    (4, 96, 3072, 16, 5, 64),            # denoiser width: 6 tiles per 16-row group
+    (3, 64, 4096, 8, 3, 64),             # fp16 with a wide alphabet
+    (2, 200, 776, 5, 4, 128),            # ragged rows and tiles, 128 states per tile
+    (2, 48, 1024, 3, 35, 64),            # 35 blobs: two launches
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-m{c[3]}-n{c[4]}-k{c[5]}")
+def test_matmul_batch_matches_oracle(orc, case):
+    key, R, C, m, n, lanes = case
+    log("decompress_matmul_batch", case)
+    wl = S.WORKLOADS[key]
+    dt = wl["dtype"]
+    blobs, xs = [], []
+    for i in range(n):
+        st, blob, _ = orc.compress(_weights(key, R, C, i), dt, wl["target_bpp"],
+                                   wl["tile_fields"], lanes=lanes)
+        assert st == 0
+        blobs.append(blob)
+        xs.append(S.iid_normal(m, C, 300 + i, sigma=1.0, dtype=dt))
+    Ys = _batch_run([GpuBlob(b) for b in blobs], xs, m)
+    for blob, x, Y in zip(blobs, xs, Ys):
+        _check(orc, blob, x, Y)
+
+
+def test_matmul_batch_deterministic_and_refusals(orc):
+    import torch
+
+    ep = ep_mod()
+    gbs = [GpuBlob(orc.compress(S.lognormal_rows(64, 1024, seed=70 + i), S.BF16, 4.0, 8192)[1])
+           for i in range(3)]
+    xs = [S.iid_normal(4, 1024, 80 + i, sigma=1.0, dtype=S.BF16) for i in range(3)]
+    a = _batch_run(gbs, xs, 4)
+    b = _batch_run(gbs, xs, 4)
+    assert all(np.array_equal(p, q) for p, q in zip(a, b))
+    d_x = dev(xs[0].view(np.uint16))
+    d_y = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call(gl, m=4):
+        return ep.ep_decompress_matmul_batch([g.d_blob for g in gl], [g.info for g in gl],
+                                             [g.d_tab for g in gl], [d_x] * len(gl), m,
+                                             [d_y] * len(gl), d_err)
+
+    assert call([]) == ep.EP_ERR_ARG                      # no blobs
+    assert call(gbs, m=65) == ep.EP_ERR_ARG
+    other_rows = GpuBlob(orc.compress(S.lognormal_rows(48, 1024, seed=9), S.BF16, 4.0, 8192)[1])
+    assert call([gbs[0], other_rows]) == ep.EP_ERR_ARG    # shapes differ
+    other_k = GpuBlob(orc.compress(S.lognormal_rows(64, 1024, seed=9), S.BF16, 4.0, 8192,
+                                   lanes=128)[1])
+    assert call([gbs[0], other_k]) == ep.EP_ERR_ARG       # states per tile differ
+    fp16 = GpuBlob(orc.compress(S.student_t_outliers(64, 1024, seed=9), S.FP16, 4.0, 8192)[1])
+    assert call([gbs[0], fp16]) == ep.EP_ERR_ARG          # containers differ
+    torch.cuda.synchronize()
+    assert int(host(d_err)[0]) == 0                       # nothing was launched
+
+
+@pytest.mark.timeout(900)
+def test_matmul_batch_full_size_denoiser(orc):
+    """All 64 matrices of the 3072 x 3072 bf16 denoiser batch, m = 16, in one call (two launches
+    of 32 blobs): each product within the bound of the oracle's fp64 product of its decode."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from gpu_util import gpu_compress
+
+    wl = S.WORKLOADS[4]
+    R, C, dt, F, nb, m = wl["rows"], wl["cols"], wl["dtype"], wl["tile_fields"], wl["batch"], 16
+    log("library compress of the 64 denoiser matrices")
+    blobs = [gpu_compress(S.workload_weights(4, index=i), dt, wl["target_bpp"], F)[0]
+             for i in range(nb)]
+    xs = [S.iid_normal(m, C, 400 + i, sigma=1.0, dtype=dt) for i in range(nb)]
+    log("batched decompress_matmul")
+    Ys = _batch_run([GpuBlob(b) for b in blobs], xs, m)
+    log("oracle products (threaded) and compare")
+    with ThreadPoolExecutor(16) as ex:
+        refs = list(ex.map(lambda i: orc.decompress_matmul(blobs[i], xs[i]), range(nb)))
+    for i, (st, Yr, B) in enumerate(refs):
+        assert st == 0
+        tol = (C + 16) * U32 * B + 1e-30
+        assert not (np.abs(Ys[i] - Yr) > tol).any(), f"matrix {i}"
