@@ -266,6 +266,7 @@ def main():
         del X
 
     single = None
+    consumer_batch = None
     if n_mat > 1:
         # the whole batch: every matrix compressed, then one batched decode per step
         single = {"us_per_matrix_single_decode": round(ms * 1e3, 3)}
@@ -310,6 +311,40 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         single["us_64_single_launches"] = round(ev0.elapsed_time(ev1) / seq_steps * 1e3, 1)
+        # the product that consumes each decoded matrix, fused for the whole batch
+        # (ep_decompress_matmul_batch) against the batched decode plus one library GEMM each
+        mc = args.consumer_m
+        if mc and dt in (S.BF16, S.FP16) and mc <= ep.EP_MM_MAX_M and C <= ep.EP_MM_MAX_COLS:
+            xs = [torch.randn(mc, C, device=dev, dtype=torch.float32).to(tdt)
+                  for _ in range(n_mat)]
+            ys = [torch.empty((mc, R), dtype=torch.float32, device=dev) for _ in range(n_mat)]
+
+            def unfused():
+                assert ep.ep_decompress_batch(bl, infos, tb, ob, err) == 0
+                for k in range(n_mat):
+                    torch.matmul(xs[k], ob[k].t())
+
+            def fused_batch():
+                assert ep.ep_decompress_matmul_batch(bl, infos, tb, xs, mc, ys, err) == 0
+
+            res = {}
+            for name, f in (("unfused_ms", unfused), ("fused_batch_ms", fused_batch)):
+                for _ in range(2):
+                    f()
+                torch.cuda.synchronize()
+                ev0.record()
+                for _ in range(seq_steps):
+                    f()
+                ev1.record()
+                torch.cuda.synchronize()
+                res[name] = round(ev0.elapsed_time(ev1) / seq_steps, 4)
+            assert int(err.item()) == 0
+            consumer_batch = {
+                "m": mc, "matrices": n_mat, **res,
+                "fused_vs_unfused": round(res["unfused_ms"] / res["fused_batch_ms"], 4),
+                "timing": "events around each form: the batched decode with one torch.matmul "
+                          "per matrix, against one ep_decompress_matmul_batch call"}
+            del xs, ys
 
     value = out_bytes / (ms * 1e-3) / 1e9
     algo_bytes = blob_bytes + out_bytes
@@ -356,6 +391,7 @@ def main():
         },
         "refine": refine,
         "consumer": consumer,
+        "consumer_batch": consumer_batch,
         "phases": phases,
         "encode": {
             "kernel": f"k_encode_tiles<{F // 512}> + offset scan + word copy",
