@@ -293,3 +293,27 @@ def test_matmul_batch_full_size_denoiser(orc):
         assert st == 0
         tol = (C + 16) * U32 * B + 1e-30
         assert not (np.abs(Ys[i] - Yr) > tol).any(), f"matrix {i}"
+
+
+def test_high_level_decompress_matmul_batch(orc):
+    import torch
+
+    ep = ep_mod()
+    cs, xbs, xs = [], [], []
+    for i in range(3):
+        w = S.lognormal_rows(128, 1024, seed=90 + i)
+        t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+        cs.append(ep.compress(t, ep.LatticeRANSConfig(target_bpp=4.0, tile_fields=8192)))
+        xb = S.iid_normal(6, 1024, 95 + i, sigma=1.0, dtype=S.BF16)
+        xbs.append(xb)
+        xs.append(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda())
+    ys = ep.decompress_matmul_batch(cs, xs)
+    torch.cuda.synchronize()
+    assert len(ys) == 3
+    for c, xb, y in zip(cs, xbs, ys):
+        assert y.shape == (6, 128) and y.dtype == torch.float32
+        _check(orc, c.blob, xb, host(y).astype(np.float64))
+    with pytest.raises(ep.EPError):
+        ep.decompress_matmul_batch(cs, xs[:2])
+    with pytest.raises(ep.EPError):
+        ep.decompress_matmul_batch(cs, [xs[0], xs[1], xs[2][:3]])
