@@ -124,8 +124,8 @@ __device__ __forceinline__ float sqdist8(const float x[8], const float p[8]) {
   return d;
 }
 
-// Returns the coset; z receives the D8 part (p - coset/2).
-__device__ __forceinline__ int e8_nearest(const float x[8], int32_t z[8]) {
+// Returns the coset; z receives the D8 part (p - coset/2) as integer-valued floats.
+__device__ __forceinline__ int e8_nearest(const float x[8], float z[8]) {
   float A[8], u[8], Bz[8], B[8];
   d8_round(x, A);
 #pragma unroll
@@ -137,7 +137,7 @@ __device__ __forceinline__ int e8_nearest(const float x[8], int32_t z[8]) {
   const float dB = sqdist8(x, B);
   const int c = (dA <= dB) ? 0 : 1;
 #pragma unroll
-  for (int i = 0; i < 8; i++) z[i] = (int32_t)(c ? Bz[i] : A[i]);
+  for (int i = 0; i < 8; i++) z[i] = c ? Bz[i] : A[i];
   return c;
 }
 
@@ -290,10 +290,18 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
 #pragma unroll
         for (int k = 0; k < 8; k++) x[k] = 0.0f;
       }
+      float zf[8];
+      int c = e8_nearest(x, zf);
+      // a coordinate outside [-32767, 32767]: one maximum over the magnitudes (integers below
+      // 2^17 here, so the fp32 compare is exact) instead of two integer compares per coordinate
+      const float zmax = fmaxf(fmaxf(fmaxf(__builtin_fabsf(zf[0]), __builtin_fabsf(zf[1])),
+                                     fmaxf(__builtin_fabsf(zf[2]), __builtin_fabsf(zf[3]))),
+                               fmaxf(fmaxf(__builtin_fabsf(zf[4]), __builtin_fabsf(zf[5])),
+                                     fmaxf(__builtin_fabsf(zf[6]), __builtin_fabsf(zf[7]))));
+      out_of_range |= zmax > 32767.0f;
       int32_t z[8];
-      int c = e8_nearest(x, z);
 #pragma unroll
-      for (int k = 0; k < 8; k++) out_of_range |= (z[k] > 32767) | (z[k] < -32767);
+      for (int k = 0; k < 8; k++) z[k] = (int32_t)zf[k];
       bad |= out_of_range;
       int32_t f[8];
 #pragma unroll
