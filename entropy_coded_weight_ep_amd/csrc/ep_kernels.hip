@@ -84,33 +84,39 @@ __global__ __launch_bounds__(64) void k_row_sumsq(const void* __restrict__ w, in
 // ------------------------------------------------------------------------------------------
 // Branch-free: every lane computes the residuals and the worst coordinate, and the move is a
 // select (an odd sum is about every other vector, so a branch would diverge in every wavefront).
+// The worst coordinate is the first whose |residual| equals the largest one: one maximum over
+// the eight magnitudes, one compare per coordinate, and the "first hit" kept in lane masks
+// (scalar ops), instead of a running compare-and-select of (residual, index).
 // The residual u - rint(u) is exact and never -0 (x - x rounds to +0), so copysign(1, r_k) is
 // the step towards u, +1 for a zero residual.
 // The coordinate sum is formed in fp32: the eight rounded values are integers of magnitude at
 // most 65537 (|x| <= 65536 is checked before), so every partial sum is exact and one conversion
-// gives the parity.
+// gives the parity (the sign of a zero partial sum does not change it).
 __device__ __forceinline__ void d8_round(const float u[8], float a[8]) {
-  float fsum = 0.0f;
   float r[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     a[i] = __builtin_rintf(u[i]);
-    fsum = __fadd_rn(fsum, a[i]);
     r[i] = __fsub_rn(u[i], a[i]);
   }
-  const int32_t sum = (int32_t)fsum;
-  int k = 0;
-  float rk = r[0];                                 // residual of the worst coordinate so far
+  float fsum = __fadd_rn(a[0], a[1]);
 #pragma unroll
-  for (int i = 1; i < 8; i++) {
-    const bool worse = __builtin_fabsf(r[i]) > __builtin_fabsf(rk);
-    rk = worse ? r[i] : rk;
-    k = worse ? i : k;
+  for (int i = 2; i < 8; i++) fsum = __fadd_rn(fsum, a[i]);
+  const bool odd = ((int32_t)fsum & 1) != 0;
+  // the largest |r|: max(a, b) = med3(a, b, 1) since every |r| is at most 1/2 (one instruction
+  // each, where fmaxf would add a canonicalisation of every operand)
+  auto mx = [](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 1.0f); };
+  const float m = mx(mx(mx(__builtin_fabsf(r[0]), __builtin_fabsf(r[1])),
+                        mx(__builtin_fabsf(r[2]), __builtin_fabsf(r[3]))),
+                     mx(mx(__builtin_fabsf(r[4]), __builtin_fabsf(r[5])),
+                        mx(__builtin_fabsf(r[6]), __builtin_fabsf(r[7]))));
+  bool done = !odd;                                // an even sum moves nothing
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const bool hit = !done && __builtin_fabsf(r[i]) == m;
+    done = done || hit;
+    a[i] = hit ? __fadd_rn(a[i], __builtin_copysignf(1.0f, r[i])) : a[i];
   }
-  k = (sum & 1) ? k : 8;                           // an even sum moves nothing
-  const float step = __builtin_copysignf(1.0f, rk);
-#pragma unroll
-  for (int i = 0; i < 8; i++) a[i] = (i == k) ? __fadd_rn(a[i], step) : a[i];
 }
 
 __device__ __forceinline__ float sqdist8(const float x[8], const float p[8]) {
