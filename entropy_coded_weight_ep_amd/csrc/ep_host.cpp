@@ -572,12 +572,27 @@ extern "C" ep_status ep_blob_parse(const void* h_blob, size_t bytes, ep_blob_inf
   // row scales must be finite (the decoder's saturating conversions assume it); a nonzero scale
   // below 2^-125 in magnitude has an inexact half, which the decoder's fused scaling needs exact
   bool tiny = false;
+  float max_alpha = 0.0f;
   for (int64_t r = 0; r < I.rows; r++) {
     float alpha;
     std::memcpy(&alpha, b + L.alpha + 4 * r, 4);
     if (!std::isfinite(alpha)) return EP_ERR_CORRUPT;
     tiny |= alpha != 0.0f && std::fabs(alpha) < 0x1p-125f;
+    max_alpha = std::max(max_alpha, std::fabs(alpha));
   }
+  // the largest |p| the tile decode can produce: a field of table 1 + 8c + k lies in
+  // [lo, lo + n - 1]; z7 = 2 f7 + parity; p = z + c/2.  (Escaped vectors, rewritten by the patch
+  // pass with its own conversion, are not bounded by this.)  Both products below are exact in
+  // double: max_alpha has 24 significant bits, max_p at most 18.
+  double max_p = 0.0;
+  for (int t = 1; t < EP_NTABLES; t++) {
+    if (I.n[t] == 0) continue;
+    const int c = (t - 1) / 8, k = (t - 1) % 8;
+    int64_t m = std::max(std::llabs((int64_t)I.lo[t]), std::llabs((int64_t)I.lo[t] + I.n[t] - 1));
+    if (k == 7) m = 2 * m + 1;
+    max_p = std::max(max_p, (double)m + 0.5 * c);
+  }
+  I.bounded = (double)max_alpha * max_p <= 448.0 ? 1u : 0u;
   const uint32_t* off = reinterpret_cast<const uint32_t*>(b + L.word_off);
   if (off[0] != 0 || (int64_t)off[I.tiles] != I.payload_words) return EP_ERR_CORRUPT;
   uint32_t maxw = 0;

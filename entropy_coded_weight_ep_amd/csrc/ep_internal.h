@@ -104,6 +104,9 @@ static_assert(sizeof(DecodeArgs) <= 4096, "kernel arguments");
 // J = 32, where it lets 3 waves per SIMD fit the registers).
 // `ring`: stream each tile's words through an LDS ring of words_stride words (a power of two)
 // instead of holding the whole tile.
+// DT may also be kFp8Bounded: an fp8 e4m3fn container whose blob is `bounded` (every decoded
+// value within +-448), converted without the saturation clamp (S = 1 only).
+constexpr int kFp8Bounded = 0x100 | EP_FP8_E4M3FN;
 template <int DT, int S>
 hipError_t launch_decode(const DecodeArgs& a, int J, bool big, bool ragged, bool slow, bool rows2,
                          bool ring, int waves, size_t lds, hipStream_t s);

@@ -149,6 +149,54 @@ def test_blob_parse_flags_tiny_scales(ep, orc, alpha, tiny):
     assert st == 0 and info2.tiny_scale == tiny
 
 
+def _decoded_points(orc, blob, info):
+    """(|p| of every decoded vector [NV, 8], |alpha| per row), from the oracle's decoded cosets
+    and fields: z7 = 2 f7 + parity(f0..f6), p = z + c/2 (design page "EntroPack lattice
+    compression", Lattice quantization and integer fields)."""
+    st, _, cos, fld = orc.decompress(blob, want_fields=True)
+    assert st == 0
+    f = fld.reshape(-1, 8).astype(np.int64)
+    z = f.copy()
+    z[:, 7] = 2 * f[:, 7] + (f[:, :7].sum(axis=1) & 1)
+    p = np.abs(z + 0.5 * cos[:, None])
+    alpha = blob[info.off_alpha:info.off_alpha + 4 * info.rows].view(np.float32)
+    return p, np.abs(alpha.astype(np.float64))
+
+
+@pytest.mark.parametrize("key", [1, "5a", "5b"])
+def test_blob_parse_bound_flag(ep, orc, key):
+    # `bounded`: every value the tile decode writes lies within +-448.  The flag's bound on |p|
+    # (from the field tables' value ranges) must cover every point the oracle's decode
+    # reconstructs; the flag is set exactly when the largest |row scale| times that bound is at
+    # most 448, which one row scale then crosses.
+    wl = S.WORKLOADS[key]
+    w = S.workload_weights(key, 32, 2048)
+    st, blob, s = orc.compress(w, wl["dtype"], wl["target_bpp"], 4096)
+    assert st == 0
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0
+    p, alpha = _decoded_points(orc, blob, info)
+    vpr = (info.cols + 7) // 8
+    assert (alpha[np.arange(len(p)) // vpr][:, None] * p).max() <= 448.0
+    assert info.bounded == 1
+    mp = 0.0
+    for t in range(1, 17):
+        if info.n[t]:
+            m = max(abs(info.lo[t]), abs(info.lo[t] + info.n[t] - 1))
+            mp = max(mp, (2 * m + 1 if (t - 1) % 8 == 7 else m) + 0.5 * ((t - 1) // 8))
+    assert p.max() <= mp
+    a_max = np.float32(448.0 / mp)                  # the largest fp32 scale the bound admits
+    while float(a_max) * mp > 448.0:
+        a_max = np.nextafter(a_max, np.float32(0))
+    assert alpha.max() <= a_max
+    for a, want in ((a_max, 1), (np.nextafter(a_max, np.float32(1e9)), 0), (np.float32(1e3), 0),
+                    (-a_max, 1), (np.float32(-1e3), 0)):
+        b = blob.copy()
+        b[info.off_alpha + 4 * 3:info.off_alpha + 4 * 4] = np.array([a], np.float32).view(np.uint8)
+        st, info2 = ep.ep_blob_parse(b)
+        assert st == 0 and info2.bounded == want, (a, want)
+
+
 @pytest.mark.parametrize("s", [0.05, 0.3, 1.0, 4.0])
 def test_estimate_matches_oracle(ep, orc, s):
     w = S.lognormal_rows(600, 512, seed=4)

@@ -443,6 +443,38 @@ def test_decode_container_edges(orc, key, shape):
     assert np.array_equal(out, ref), f"{int(np.sum(out != ref))} elements differ"
 
 
+@pytest.mark.parametrize("shape", [(32, 2048), (64, 28672)], ids=lambda c: f"{c[0]}x{c[1]}")
+def test_fp8_bounded_and_clamped_decodes(orc, shape):
+    """An fp8 blob whose decoded values provably stay within +-448 (`bounded`) is converted
+    without the saturation clamp; raising one row scale past the bound sends the same blob
+    through the clamped conversion.  Both must equal the oracle's decode bit for bit, at a
+    16384-field tile shape (32 vectors per lane, the two-workgroups-per-CU ring launch)."""
+    import entropy_coded_weight_ep_amd as ep
+
+    R, C = shape
+    log("fp8 bounded / clamped", shape)
+    wl = S.WORKLOADS["5a"]
+    w = S.workload_weights("5a", R, C)
+    st, blob, s = orc.compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"])
+    assert st == 0
+    st, info = ep.ep_blob_parse(blob)
+    assert st == 0 and info.bounded == 1
+    bad = blob.copy()
+    for r in range(0, R, 7):                        # a few rows far past the bound
+        bad[info.off_alpha + 4 * r:info.off_alpha + 4 * r + 4] = \
+            np.array([(-1.0) ** r * 300.0], np.float32).view(np.uint8)
+    st, info_bad = ep.ep_blob_parse(bad)
+    assert st == 0 and info_bad.bounded == 0
+    for b in (blob, bad):
+        st, ref, _, _ = orc.decompress(b)
+        assert st == 0
+        err, out = GpuBlob(b).decode()
+        assert err == 0
+        assert np.array_equal(out, ref), f"{int(np.sum(out != ref))} elements differ"
+    # the clamped blob really saturates somewhere
+    assert np.any((ref.view(np.uint8) & 0x7F) == 0x7E)
+
+
 def test_blob_with_nonfinite_scale_is_rejected(orc):
     import entropy_coded_weight_ep_amd as ep
 
