@@ -35,6 +35,8 @@ constexpr int kDecWaves = 16;
 // Compute units of an MI355X and LDS bytes per CU, for the decoder's workgroup size choice.
 constexpr int64_t kCUs = 256;
 constexpr int64_t kLdsPerCU = 160 * 1024;
+// The decoder's word ring is followed by a copy of its first 64 words (16-bit each).
+constexpr uint32_t kRingMirrorBytes = 128;
 
 // The decode tables of one blob (EP_DEC_TABLE_BYTES of device memory).
 struct DecTables {

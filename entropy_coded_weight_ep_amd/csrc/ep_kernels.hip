@@ -782,8 +782,10 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   // choice that keeps the most tiles resident at once; ties go to the linear layout, then to the
   // less crowded CU (the smaller workgroup, spread over more CUs, unless it would share CUs) of
   // at least 4 waves.
-  auto lds_of = [&](int w, uint32_t stride) -> size_t {
-    return (size_t)(big ? kWideTop : kNarTop) + (size_t)w * ((size_t)256 * S + (size_t)stride * 2);
+  // (a ring region also holds the copy of its first 64 words)
+  auto lds_of = [&](int w, uint32_t stride, bool rg) -> size_t {
+    return (size_t)(big ? kWideTop : kNarTop) +
+           (size_t)w * ((size_t)256 * S + (size_t)stride * 2 + (rg ? kRingMirrorBytes : 0u));
   };
   // waves per SIMD the decoder's registers allow: 8, 4 and 4 for 8, 16 and 32 vectors per lane
   // (2 at 32 with wide alphabets, whose fields take 16 bits each, or 3 when every row holds a
@@ -812,9 +814,9 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
     const uint32_t st = lay == 0 ? lin_stride : (lay == 1 ? ring_stride : ring_half);
     if (rg && layout == 0 && st >= lin_stride) continue;
     for (const int w : {16, 12, 8, 4, 2, 1}) {
-      if (w > max_waves || (int64_t)lds_of(w, st) > kLdsPerCU) continue;
+      if (w > max_waves || (int64_t)lds_of(w, st, rg) > kLdsPerCU) continue;
       const int64_t per_cu =
-          std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, st), waves_per_cu / w);
+          std::min<int64_t>(kLdsPerCU / (int64_t)lds_of(w, st, rg), waves_per_cu / w);
       const int64_t grid = (total_tiles + w - 1) / w;
       const int64_t resident = std::min(std::min(grid, kCUs * per_cu) * w, total_tiles);
       // the most waves one CU holds at once: a smaller workgroup that still ends up two to a CU
@@ -832,11 +834,11 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
   if (waves == 0) return EP_ERR_VERSION;             // one tile's words do not fit in LDS
   // 32 vectors per lane with byte fields: 4 waves per SIMD, bound by VALU issue, and a 16-wave
   // workgroup's waves reach its phase barriers far apart while their SIMDs idle.  Two 8-wave
-  // workgroups per CU on the ring layout (one VALU op more per step) let one workgroup decode
-  // while the other waits at a barrier (8192 x 28672 fp8: 195 -> 188 us, measured); taken when
-  // they keep as many tiles resident.
+  // workgroups per CU, which LDS holds only with the ring layout, let one workgroup decode
+  // while the other waits at a barrier (measured at 8192 x 28672 fp8: 195 -> 188 us); taken
+  // when they keep as many tiles resident.
   if (J == 32 && !big && S == 1 && layout == 0 && !stamps && waves == 16 && !ring) {
-    const size_t l8 = lds_of(8, ring_stride);
+    const size_t l8 = lds_of(8, ring_stride, true);
     const int64_t per_cu = std::min<int64_t>(kLdsPerCU / (int64_t)l8, waves_per_cu / 8);
     const int64_t grid8 = (total_tiles + 7) / 8;
     const int64_t resident = std::min(std::min(grid8, kCUs * per_cu) * 8, total_tiles);
@@ -846,7 +848,7 @@ static ep_status decode_blobs(int n, const void* const* d_blobs, const ep_blob_i
       stride = ring_stride;
     }
   }
-  const size_t lds = lds_of(waves, stride);
+  const size_t lds = lds_of(waves, stride, ring);
   const uint32_t V = (uint32_t)i0.tile_fields / 8;
 
   DecodeArgs a;
