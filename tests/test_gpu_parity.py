@@ -315,6 +315,44 @@ def test_decode_batch_matches_oracle(orc):
         assert np.array_equal(got, ref)
 
 
+def test_decode_fp8_batch_mixed_bounds(orc):
+    """A batch of fp8 blobs at 16384-field tiles where some blobs are bounded (values within
+    +-448) and some are not: the whole batch takes the clamped conversion, and a batch of
+    bounded blobs alone the unclamped one; both must write what the oracle writes."""
+    import torch
+
+    ep = ep_mod()
+    wl = S.WORKLOADS["5a"]
+    blobs, refs = [], []
+    for i in range(6):
+        w = S.workload_weights("5a", 16, 4096, i)
+        st, blob, s = orc.compress(w, wl["dtype"], wl["target_bpp"], wl["tile_fields"])
+        assert st == 0
+        if i % 3 == 2:                                  # one row scale far past the bound
+            st, info = ep.ep_blob_parse(blob)
+            assert st == 0
+            blob = blob.copy()
+            blob[info.off_alpha:info.off_alpha + 4] = np.array([500.0], np.float32).view(np.uint8)
+        st, ref, _, _ = orc.decompress(blob)
+        assert st == 0
+        blobs.append(GpuBlob(blob))
+        refs.append(ref)
+    assert sorted({b.info.bounded for b in blobs}) == [0, 1]
+    log("decode fp8 batch, mixed bounds")
+    for sel in (range(6), [i for i in range(6) if blobs[i].info.bounded]):
+        bs = [blobs[i] for i in sel]
+        outs = [torch.zeros(b.out_bytes(), dtype=torch.uint8, device="cuda") for b in bs]
+        d_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        st = ep.ep_decompress_batch([b.d_blob for b in bs], [b.info for b in bs],
+                                    [b.d_tab for b in bs], outs, d_err)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert int(d_err.item()) == 0
+        for i, o in zip(sel, outs):
+            got = o.cpu().numpy().reshape(blobs[i].info.rows, blobs[i].info.cols)
+            assert np.array_equal(got, refs[i].view(np.uint8))
+
+
 def test_decode_batch_rejects_mixed_containers(orc):
     import torch
 
