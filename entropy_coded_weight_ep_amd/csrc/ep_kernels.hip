@@ -406,6 +406,99 @@ __global__ __launch_bounds__(kQThreads) void k_quantize_e8(
 }
 
 // ------------------------------------------------------------------------------------------
+// Row statistics in any order, for the containers where that gives the left-to-right fp64 sums
+// bit for bit.  An e4m3fn value is an integer multiple of 2^-9 below 2^18 of them (448 = 229376
+// x 2^-9); an int8 value is an integer.  So each square w^2 and each product w p (p = h/2, |h| <
+// 2^16) is an integer multiple of a fixed quantum (2^-18, 2^-10; 1, 1/2) of at most 36 bits, and
+// every partial sum of a row of at most 2^17 elements stays below 2^53 quanta: exact in fp64,
+// whatever the order (finite inputs; a NaN row sums to a NaN either way).  One 256-thread
+// workgroup per row; each thread sums its strided vectors, then wavefront shuffles and the four
+// wavefronts' partial sums.  kOrderFreeCols bounds the fp8 row width (int8 rows are exact at any
+// width the library accepts).
+// ------------------------------------------------------------------------------------------
+constexpr int64_t kOrderFreeCols = (int64_t)1 << 17;
+constexpr int kRowThreads = 256;
+
+static inline bool order_free_host(int dt, int64_t cols) {
+  return dt == EP_INT8 || (dt == EP_FP8_E4M3FN && cols <= kOrderFreeCols);
+}
+
+template <typename T>
+__device__ __forceinline__ T row_reduce(T acc, T* part) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+template <int DT, bool PAD>
+__global__ __launch_bounds__(kRowThreads) void k_row_sumsq_any(const void* __restrict__ w,
+                                                               int64_t rows, int64_t cols,
+                                                               double* __restrict__ out) {
+  static_assert(DT == EP_INT8 || DT == EP_FP8_E4M3FN, "order-free containers only");
+  __shared__ double part[kRowThreads / 64];
+  const int64_t r = blockIdx.x;
+  const int64_t vpr = (cols + 7) / 8;
+  double acc = 0.0;
+  for (int64_t m = threadIdx.x; m < vpr; m += kRowThreads) {
+    float x[8];
+    raw_widen<DT>(row_vec<DT, PAD>(w, r, cols, vpr, m), x);   // padding widens to 0
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const double v = (double)x[i];
+      acc = __dadd_rn(acc, __dmul_rn(v, v));
+    }
+  }
+  const double sum = row_reduce(acc, part);
+  if (threadIdx.x == 0) out[r] = sum;
+}
+
+template <int DT, bool PAD>
+__global__ __launch_bounds__(kRowThreads) void k_row_lsq_any(
+    const void* __restrict__ w, int64_t rows, int64_t cols, const uint8_t* __restrict__ coset,
+    const int16_t* __restrict__ fields, double* __restrict__ num, int64_t* __restrict__ den4) {
+  static_assert(DT == EP_INT8 || DT == EP_FP8_E4M3FN, "order-free containers only");
+  __shared__ double part[kRowThreads / 64];
+  __shared__ long long part4[kRowThreads / 64];
+  const int64_t r = blockIdx.x;
+  const int64_t vpr = (cols + 7) / 8, v_row = r * vpr;
+  const uint4* fv = reinterpret_cast<const uint4*>(fields);
+  double acc = 0.0;
+  long long d4 = 0;
+  for (int64_t m = threadIdx.x; m < vpr; m += kRowThreads) {
+    float x[8];
+    raw_widen<DT>(row_vec<DT, PAD>(w, r, cols, vpr, m), x);
+    const uint4 fq = fv[v_row + m];
+    const int32_t c = (int32_t)coset[v_row + m];
+    const uint32_t q[4] = {fq.x, fq.y, fq.z, fq.w};
+    int32_t f[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      f[2 * i] = (int32_t)(int16_t)(q[i] & 0xFFFFu);
+      f[2 * i + 1] = (int32_t)q[i] >> 16;
+    }
+    int32_t par = 0;
+#pragma unroll
+    for (int i = 0; i < 7; i++) par ^= f[i];
+    f[7] = 2 * f[7] + (par & 1);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if (PAD && 8 * m + i >= cols) break;            // padding: not a weight
+      const int64_t h = 2 * (int64_t)f[i] + c;
+      acc = __dadd_rn(acc, __dmul_rn((double)x[i], (double)h * 0.5));
+      d4 += h * h;
+    }
+  }
+  const double sum = row_reduce(acc, part);
+  const long long s4 = row_reduce(d4, part4);
+  if (threadIdx.x == 0) {
+    num[r] = sum;
+    den4[r] = s4;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Row least-squares terms: one lane per row, streamed like the row sums (weights, fields and
 // cosets of the next kRowChunk vectors loaded while the current ones are summed).
 // num = sum w * p (fp64, left to right; each product exact), den4 = sum (2p)^2 (int64).
@@ -600,8 +693,20 @@ extern "C" ep_status ep_row_sumsq(const void* d_w, int32_t dtype, int64_t rows, 
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
   if (!shape_fits(rows, cols)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((rows + 63) / 64));
   const bool pad = cols % 8 != 0;
+  if (rows > 0 && order_free_host(dtype, cols)) {      // one workgroup per row, any order
+    const dim3 rgrid((unsigned)rows);
+    if (dtype == EP_INT8)
+      pad ? k_row_sumsq_any<EP_INT8, true><<<rgrid, kRowThreads, 0, s>>>(d_w, rows, cols, d_out)
+          : k_row_sumsq_any<EP_INT8, false><<<rgrid, kRowThreads, 0, s>>>(d_w, rows, cols, d_out);
+    else
+      pad ? k_row_sumsq_any<EP_FP8_E4M3FN, true><<<rgrid, kRowThreads, 0, s>>>(d_w, rows, cols,
+                                                                              d_out)
+          : k_row_sumsq_any<EP_FP8_E4M3FN, false><<<rgrid, kRowThreads, 0, s>>>(d_w, rows, cols,
+                                                                               d_out);
+    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+  }
+  const dim3 grid((unsigned)((rows + 63) / 64));
 #define EP_S(DT)                                                                              \
   (pad ? k_row_sumsq<DT, true><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out)                    \
        : k_row_sumsq<DT, false><<<grid, 64, 0, s>>>(d_w, rows, cols, d_out))
@@ -677,8 +782,20 @@ extern "C" ep_status ep_row_lsq(const void* d_w, int32_t dtype, int64_t rows, in
   if (!valid_dtype(dtype)) return EP_ERR_DTYPE;
   if (!shape_fits(rows, cols)) return EP_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((rows + 63) / 64));
   const bool pad = cols % 8 != 0;
+  if (rows > 0 && order_free_host(dtype, cols)) {      // one workgroup per row, any order
+    const dim3 rgrid((unsigned)rows);
+#define EP_LA(DT, PAD)                                                                        \
+  k_row_lsq_any<DT, PAD><<<rgrid, kRowThreads, 0, s>>>(d_w, rows, cols, d_coset, d_fields,     \
+                                                       d_num, d_den4)
+    if (dtype == EP_INT8)
+      pad ? EP_LA(EP_INT8, true) : EP_LA(EP_INT8, false);
+    else
+      pad ? EP_LA(EP_FP8_E4M3FN, true) : EP_LA(EP_FP8_E4M3FN, false);
+#undef EP_LA
+    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+  }
+  const dim3 grid((unsigned)((rows + 63) / 64));
 #define EP_L1(DT, PAD)                                                                        \
   k_row_lsq<DT, PAD><<<grid, 64, 0, s>>>(d_w, rows, cols, d_coset, d_fields, d_num, d_den4)
 #define EP_L(DT) (pad ? EP_L1(DT, true) : EP_L1(DT, false))

@@ -39,6 +39,33 @@ def test_row_sumsq(orc, dtype, shape):
     assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
 
 
+@pytest.mark.parametrize("dtype", [S.FP8, S.INT8])
+@pytest.mark.parametrize("cols", [131072, 131080, 28672 + 5])
+def test_row_sumsq_wide_extremes(orc, dtype, cols):
+    """fp8 and int8 rows are summed by one workgroup per row in any order (every partial sum
+    is exact in fp64 up to 2^17 fp8 elements; wider fp8 rows take the left-to-right kernel).
+    Rows of extreme magnitudes at and past that width, and a ragged one: the largest value, the
+    smallest subnormal and zeros interleaved, alternating signs, and random codes, must give the
+    oracle's sums bit for bit."""
+    log("row_sumsq wide", dtype, cols)
+    g = np.random.Generator(np.random.PCG64(29))
+    big = 448.0 if dtype == S.FP8 else -128.0
+    tiny = 2.0 ** -9 if dtype == S.FP8 else 1.0
+    rows = [np.tile(np.array([big, tiny, 0.0, -big], np.float32), cols // 4 + 1)[:cols],
+            np.full(cols, big, np.float32),
+            np.where(np.arange(cols) % 2 == 0, tiny, -tiny).astype(np.float32),
+            g.laplace(0.0, 30.0 if dtype == S.FP8 else 40.0, cols).astype(np.float32)]
+    x = np.stack(rows)
+    if dtype == S.INT8:
+        x = np.clip(np.rint(x), -128, 127)
+    else:
+        x = np.clip(x, -448.0, 448.0)                 # finite codes only
+    w = S.cast_container(x, dtype)
+    got = gpu_row_sumsq(w, dtype)
+    ref = orc.row_sumsq(w, dtype)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("s", [0.03, 0.4, 2.5])
 def test_quantize_and_histogram(orc, dtype, s):
